@@ -1,0 +1,129 @@
+"""Pins for the oracle's full layer: brute-force dense evaluation of every
+expert on every token masked by the routing, closed forms of SwiGLU and the
+bf16 rounding, the pages' shape constants, and the dense-layer special case."""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import synth
+from oracle import ffn, route
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    s = synth.TINY
+    x = synth.bf16_bits_to_f32(synth.gen_x(s))
+    wr = synth.bf16_bits_to_f32(synth.gen_router_w(s))
+    experts = [ffn.quantize_expert(*synth.gen_expert_w(s, e)) for e in range(s.n_experts + 1)]
+    return s, x, wr, experts
+
+
+def _dense_masked(s, x, experts, idx, w):
+    """Every expert on every token; each output weighted by the token's routing
+    weight for that expert, or 0 when the expert was not chosen."""
+    from oracle import quant
+    x_q, x_s = quant.quant_1x128(x)
+    mask = np.zeros((x.shape[0], s.n_experts))
+    for t in range(x.shape[0]):
+        for j in range(s.top_k):
+            mask[t, idx[t, j]] = float(w[t, j])
+    out = np.zeros(x.shape, np.float64)
+    for e in range(s.n_experts):
+        y = ffn.expert_forward(x_q, x_s, experts[e])["y"]     # per-row quantisation: tokens are independent
+        out += mask[:, e:e + 1] * y
+    out += ffn.expert_forward(x_q, x_s, experts[s.n_experts])["y"]
+    return out
+
+
+@pytest.mark.parametrize("bias_scale", [0.0, 0.5])
+def test_tiny_layer_equals_dense_masked_evaluation(tiny, bias_scale):
+    s, x, wr, experts = tiny
+    bias = synth.gen_bias(s.n_experts, scale=bias_scale) if bias_scale else None
+    r = ffn.moe_ffn(x, s.n_experts, s.top_k, s.n_group, s.topk_group, lambda e: experts[e], w_router=wr, bias=bias)
+    want = _dense_masked(s, x, experts, r["topk_idx"], r["topk_w"])
+    assert np.allclose(r["out_f64"], want, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r["out"], ffn.round_bf16(want))
+
+
+def test_given_scores_replace_the_router(tiny):
+    s, x, wr, experts = tiny
+    sc = synth.gen_scores(s.tokens, s.n_experts, cfg_id=9)
+    r = ffn.moe_ffn(x, s.n_experts, s.top_k, s.n_group, s.topk_group, lambda e: experts[e], scores=sc)
+    idx, w = route.select(sc, None, s.n_group, s.topk_group, s.top_k)
+    assert np.array_equal(r["topk_idx"], idx)
+    want = _dense_masked(s, x, experts, idx, w)
+    assert np.allclose(r["out_f64"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_token_subset_independence(tiny):
+    s, x, wr, experts = tiny
+    full = ffn.moe_ffn(x, s.n_experts, s.top_k, s.n_group, s.topk_group, lambda e: experts[e], w_router=wr)
+    sub = [3, 17, 40]
+    part = ffn.moe_ffn(x[sub], s.n_experts, s.top_k, s.n_group, s.topk_group, lambda e: experts[e], w_router=wr)
+    assert np.array_equal(part["out"], full["out"][sub])
+
+
+def test_dense_layer_special_case():
+    s = synth.MoeShape("dense_small", 2, 8, 256, 0, 0, 0, 1, 384, 1, 1)
+    x = synth.bf16_bits_to_f32(synth.gen_x(s))
+    ex = ffn.quantize_expert(*synth.gen_expert_w(s, 0))
+    r = ffn.moe_ffn(x, 0, 0, 1, 1, lambda e: ex)
+    from oracle import quant
+    x_q, x_s = quant.quant_1x128(x)
+    assert np.array_equal(r["out"], ffn.round_bf16(ffn.expert_forward(x_q, x_s, ex)["y"]))
+
+
+def test_swiglu_closed_forms():
+    z = np.array([0.0, 1.0, -1.0, 40.0, -40.0, 2.5])
+    assert ffn.silu(z)[0] == 0.0
+    assert ffn.silu(z)[1] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert ffn.silu(z)[3] == pytest.approx(40.0, rel=1e-15)
+    assert abs(ffn.silu(z)[4]) < 1e-15
+    r = np.random.default_rng(0).standard_normal(1000) * 4
+    assert np.allclose(ffn.silu(r), r * expit(r), rtol=1e-14, atol=1e-300)
+    assert np.allclose(ffn.silu(r) - ffn.silu(-r), r, rtol=1e-13, atol=1e-13)   # silu(z) - silu(-z) = z
+
+
+def test_round_bf16_matches_library_cast():
+    r = np.random.default_rng(1)
+    v = (r.standard_normal(200000) * np.exp2(r.integers(-20, 20, 200000))).astype(np.float32)
+    lib = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ffn.round_bf16(v.astype(np.float64)), lib)
+    # fp64 inputs just above a bf16 midpoint round up (no double rounding through fp32)
+    mid = 1.0 + 2.0 ** -8
+    assert ffn.round_bf16(np.array([mid]))[0] == 1.0
+    assert ffn.round_bf16(np.array([mid + 2.0 ** -40]))[0] == np.float32(1.0 + 2.0 ** -7)
+
+
+def test_page_shape_constants():
+    s = synth.V3_PREFILL
+    # DeepSeek-R1 card, "Every architecture field"
+    assert (s.hidden, s.n_experts, s.top_k, s.inter, s.n_shared, s.inter_shared) == (7168, 256, 8, 2048, 1, 2048)
+    assert synth.DENSE_FFN.inter_shared == 18432
+    # "9 out of 257 (1 shared)" active experts (onlylabs, table in "More Aggressive Mixture-of-Expert")
+    assert s.top_k + s.n_shared == 9 and s.n_experts + s.n_shared == 257
+    # a gated expert holds three matrices: 3 * 7168 * 2048 codes (the page's 29.36M counts two)
+    assert 3 * 7168 * 2048 == 44_040_192 and 2 * 7168 * 2048 == 29_360_128
+    assert s.expert_bytes(2048) == 44_040_192 + 4 * (32 * 56 + 56 * 16)
+    # FLOPs of one MoE layer per token: 9 experts x 3 matrices x 2 FLOP per MAC
+    assert synth.with_tokens(s, 1).fp8_flops() == 9 * 6 * 7168 * 2048
+
+
+def test_fp8_fidelity_informational(tiny):
+    """parity unpinned: the pages' statement of FP8 accuracy against bf16 is cut
+    off, so this only reports the layer's error against unquantised fp64 math."""
+    s, x, wr, experts = tiny
+    r = ffn.moe_ffn(x, s.n_experts, s.top_k, s.n_group, s.topk_group, lambda e: experts[e], w_router=wr)
+    ref = np.zeros_like(r["out_f64"])
+    for t in range(s.tokens):
+        for e, wt in list(zip(r["topk_idx"][t], r["topk_w"][t])) + [(s.n_experts, 1.0)]:
+            w13, w2 = synth.gen_expert_w(s, int(e))
+            gu = x[t].astype(np.float64) @ w13.astype(np.float64).T
+            h = ffn.silu(gu[:s.inter]) * gu[s.inter:]
+            ref[t] += float(wt) * (h @ w2.astype(np.float64).T)
+    rel = np.linalg.norm(r["out_f64"] - ref) / np.linalg.norm(ref)
+    print(f"FP8 layer vs unquantised fp64: relative L2 {rel:.3e}")
+    assert rel < 0.2
