@@ -1,0 +1,269 @@
+"""Benchmark of the blockwise-FP8 MoE FFN forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_decode|v3_prefill|v3_skew|dense_ffn|tiny]
+
+A step is one moe_ffn_forward (all stages: x quantisation, router GEMM +
+sigmoid, group-limited top-k, permutation, gate/up grouped GEMM with fused
+SwiGLU + requantisation, down grouped GEMM, combine/cast) over one batch of
+seeded synthetic tokens already resident in HBM, with random-init weights of
+the DeepSeek-V3 layer shapes (weights are drawn on the device and quantised
+with the library's own 128x128 block quantiser before timing).  The default
+workload is the V3-shape decode step (T=64).
+
+Prints one JSON line.  ``roofline`` describes the dominant kernel (the gate/up
+grouped GEMM) from HIP events recorded on the launch stream between the
+library's stages; ``cpu_baseline`` times the CPU oracle on a bounded token
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (no sparsity)
+METRIC = "MoE-layer tokens/s + FP8 TFLOP/s (% MFMA peak / % HBM peak) at V3 shapes"
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (events are recorded by the library itself)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> ctypes.c_void_p:
+        e = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream) -> None:
+        assert self.rt.hipEventRecord(e, stream) == 0
+
+    def sync(self, e) -> None:
+        assert self.rt.hipEventSynchronize(e) == 0
+
+    def ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return float(f.value)
+
+    def destroy(self, e) -> None:
+        self.rt.hipEventDestroy(e)
+
+
+def build_layer(shape, dev):
+    """Device weights of the layer: fp32 draws quantised by fp8_quant_128x128 in place."""
+    import torch
+
+    import sparse_moe_ffn_sigmoid_amd as moe
+    import synth
+    E, d = shape.n_experts, shape.hidden
+    kw = {}
+    if E:
+        W = shape.inter
+        kw["w13_q"] = torch.empty((E, 2 * W, d), dtype=torch.uint8, device=dev)
+        kw["w13_s"] = torch.empty((E, 2 * W // 128, d // 128), dtype=torch.float32, device=dev)
+        kw["w2_q"] = torch.empty((E, d, W), dtype=torch.uint8, device=dev)
+        kw["w2_s"] = torch.empty((E, d // 128, W // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            moe.fp8_quant_128x128(synth.torch_expert_weight(shape, e, "w13", dev), q=kw["w13_q"][e], s=kw["w13_s"][e])
+            moe.fp8_quant_128x128(synth.torch_expert_weight(shape, e, "w2", dev), q=kw["w2_q"][e], s=kw["w2_s"][e])
+        wr = synth.gen_router_w(shape)
+        import numpy as np
+        kw["w_router"] = torch.from_numpy(wr.view(np.int16)).to(dev).view(torch.bfloat16)
+        if shape.skewed:
+            kw["bias"] = torch.from_numpy(synth.skew_bias()).to(dev)
+    if shape.n_shared:
+        a, b = moe.fp8_quant_128x128(synth.torch_expert_weight(shape, E, "w13", dev))
+        c, e_ = moe.fp8_quant_128x128(synth.torch_expert_weight(shape, E, "w2", dev))
+        kw.update(sh_w13_q=a, sh_w13_s=b, sh_w2_q=c, sh_w2_s=e_)
+    torch.cuda.synchronize()
+    return moe.MoeWeights(**kw)
+
+
+def algorithmic_bytes(shape, touched: int) -> dict:
+    """Bytes the method must move (codes + scales of experts with load > 0 and the shared
+    expert, router weights and bias, x in and the output, both bf16)."""
+    d = shape.hidden
+    routed = touched * shape.expert_bytes(shape.inter) if shape.n_experts else 0
+    shared = shape.expert_bytes(shape.inter_shared) if shape.n_shared else 0
+    router = shape.n_experts * d * 2 + shape.n_experts * 4
+    io = 2 * shape.tokens * d * 2
+    w13 = lambda width: 2 * width * d + 4 * (2 * width // 128) * (d // 128)  # noqa: E731
+    gate_up = touched * w13(shape.inter) + (w13(shape.inter_shared) if shape.n_shared else 0)
+    gate_up += shape.tokens * (d + 4 * d // 128)                              # x codes + scales in
+    rows = shape.tokens * (shape.top_k + shape.n_shared)
+    width = shape.inter if shape.n_experts else shape.inter_shared
+    gate_up += rows * (width + 4 * width // 128)                              # h codes + scales out
+    return {"layer": routed + shared + router + io, "gate_up": gate_up}
+
+
+def cpu_baseline(shape, x_bits, n_tokens: int) -> dict:
+    """The CPU oracle, as it stands, on the first n_tokens of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import ffn, route
+    x = synth.bf16_bits_to_f32(x_bits[:n_tokens])
+    wr = synth.bf16_bits_to_f32(synth.gen_router_w(shape)) if shape.n_experts else None
+    bias = synth.skew_bias() if shape.skewed else None
+    need = [shape.n_experts] if shape.n_shared else []
+    if shape.n_experts:
+        sc = route.sigmoid_scores(route.router_logits(x, wr))
+        idx, _ = route.select(sc, bias, shape.n_group, shape.topk_group, shape.top_k)
+        need += sorted(set(int(e) for e in np.unique(idx)))
+    dev = torch.device("cuda:0")
+    experts = {}
+    from concurrent.futures import ThreadPoolExecutor
+    host = {e: (synth.torch_expert_weight(shape, e, "w13", dev).cpu().numpy(),
+                synth.torch_expert_weight(shape, e, "w2", dev).cpu().numpy()) for e in need}
+    with ThreadPoolExecutor(16) as ex:          # oracle-side weight quantisation: preparation, not timed
+        for e, q in ex.map(lambda e: (e, ffn.quantize_expert(*host[e])), need):
+            experts[e] = q
+    del host
+    t0 = time.perf_counter()
+    ffn.moe_ffn(x, shape.n_experts, shape.top_k, shape.n_group, shape.topk_group, experts.__getitem__, w_router=wr,
+                bias=bias, n_shared=shape.n_shared)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of {shape.name} (T={shape.tokens}), {len(need)} experts; "
+                      f"{dt:.1f} s of numpy fp64 on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_decode")
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deterministic", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_ffn_sigmoid_amd as moe
+    import synth
+    from sparse_moe_ffn_sigmoid_amd import _lib
+
+    shape = synth.SHAPES[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] {shape.name}: building weights on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    t_build = time.perf_counter()
+    weights = build_layer(shape, dev)
+    cfg = moe.MoeConfig.of(shape)
+    x_bits = synth.gen_x(shape)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    T = shape.tokens
+    ws = moe.alloc_workspace(T, cfg, dev)
+    out = torch.empty_like(x)
+    idx = torch.empty((T, max(shape.top_k, 1)), dtype=torch.int32, device=dev)
+    print(f"[bench] weights ready in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
+
+    lib = _lib.load()
+    hip = HipEvents()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    c, wc = cfg.c(), weights.c()
+    flags = moe.MOE_FWD_DETERMINISTIC if args.deterministic else 0
+    NEV = _lib.MOE_FWD_STAGE_EVENTS
+    evs = [[hip.create() for _ in range(NEV)] for _ in range(args.steps)]
+    ev_arrays = [(ctypes.c_void_p * NEV)(*[e.value for e in row]) for row in evs]
+
+    def step(ev_arr):
+        st = lib.moe_ffn_forward_stages(
+            ctypes.c_void_p(x.data_ptr()), T, ctypes.byref(c), ctypes.byref(wc), ctypes.c_void_p(ws.data_ptr()),
+            ws.numel(), ctypes.c_void_p(out.data_ptr()), None,
+            ctypes.c_void_p(idx.data_ptr()) if shape.n_experts else None, None, flags, ev_arr,
+            NEV if ev_arr is not None else 0, stream)
+        if st != 0:
+            raise RuntimeError(f"moe_ffn_forward_stages: {lib.moe_last_error().decode()}")
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t_a, t_b = hip.create(), hip.create()
+    wall0 = time.perf_counter()
+    hip.record(t_a, stream)
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    hip.record(t_b, stream)
+    hip.sync(t_b)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = hip.ms(t_a, t_b) / args.steps
+    names = ["quant_x", "route_permute", "gate_up_gemm", "down_gemm", "combine"]
+    stage = {n: float(np.mean([hip.ms(evs[i][j], evs[i][j + 1]) for i in range(args.steps)]))
+             for j, n in enumerate(names)}
+
+    if shape.n_experts:
+        loads = np.bincount(idx.cpu().numpy().reshape(-1), minlength=shape.n_experts)
+        touched = int((loads > 0).sum())
+    else:
+        loads = np.zeros(0)
+        touched = 0
+    nbytes = algorithmic_bytes(shape, touched)
+    flops = shape.fp8_flops()
+    t_s = ms_step / 1e3
+    tflops = flops / t_s / 1e12
+    hbm_gbs = nbytes["layer"] / t_s / 1e9
+    gate_up_flops = 2.0 * shape.tokens * (shape.top_k + shape.n_shared) * shape.hidden * 2 * (
+        shape.inter if shape.n_experts else shape.inter_shared)
+    t_gu = stage["gate_up_gemm"] / 1e3
+    ai = gate_up_flops / nbytes["gate_up"]
+    if ai < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": nbytes["gate_up"] / t_gu / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gate_up_flops / t_gu / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_kernel (gate/up, SwiGLU+requant epilogue)"
+    roof["avg_ms"] = stage["gate_up_gemm"]
+    attainable = max(flops / (FP8_PEAK_TFLOPS * 1e12), nbytes["layer"] / (HBM_PEAK_GBS * 1e9))
+
+    res = {
+        "metric": METRIC, "value": T / t_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": shape.name, "tokens": T, "hidden": shape.hidden, "inter": shape.inter,
+                   "n_experts": shape.n_experts, "top_k": shape.top_k, "n_shared": shape.n_shared,
+                   "inter_shared": shape.inter_shared, "n_group": shape.n_group, "topk_group": shape.topk_group,
+                   "parallelism": "single GPU"},
+        "fp8_tflops": tflops, "pct_fp8_mfma_peak": 100 * tflops / FP8_PEAK_TFLOPS,
+        "hbm_gbs_algorithmic": hbm_gbs, "pct_hbm_peak": 100 * hbm_gbs / HBM_PEAK_GBS,
+        "frac_attainable_roofline": attainable / t_s, "stages_ms": stage, "wall_s_timed": wall,
+        "experts_touched": touched,
+        "load_max_over_mean": float(loads.max() / loads.mean()) if loads.size else None,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(shape, x_bits, min(args.cpu_tokens, T))
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

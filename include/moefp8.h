@@ -1,0 +1,222 @@
+/*
+ * moefp8.h - C ABI of libmoefp8.so: the forward pass of a DeepSeek-V3/R1-shaped
+ * Mixture-of-Experts FFN layer in blockwise FP8 on one AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [R1 card]   llm-architectures-explained, "DeepSeek-R1", "Every architecture field":
+ *               d_model 7168, 256 routed experts, 8 active, d_expert 2048, gated
+ *               experts, 1 shared expert of width 2048, dense first layers d_ff 18432.
+ *   [arch blog] onlylabs, "DeepSeek v3 and R1 Model Architecture", "Architecture
+ *               Overview" (SwiGLU), "More Aggressive Mixture-of-Expert" (9 of 257
+ *               active, 1 shared), "Structural change" (shared expert always on),
+ *               "Local Balanced Routing to Experts" (affinity gating, routing-only
+ *               bias), FP8 headings "Fine granularity quantization", "More Mantissa
+ *               bits of fp8", "Better Accumulation Precision", "Online Quantization".
+ *   [aguasto]   aguasto, "DeepSeek-R1" record, "Quantization" (blockwise FP8).
+ *
+ * Conventions for every call:
+ *   - Returns MOE_OK (0) or a negative status; moe_status_string() names it and
+ *     moe_last_error() gives a message (thread-local, valid until the next call
+ *     on the same thread).
+ *   - Every array argument is a DEVICE pointer, allocated and owned by the
+ *     caller; the library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work and return; nothing synchronises the host.
+ *   - Shapes and pointers are checked on the host before anything is enqueued;
+ *     a failed check enqueues nothing.  Device data (expert ids, offsets) is
+ *     trusted: out-of-range ids are undefined behaviour.
+ *   - Layouts are row-major.  FP8 means OCP E4M3FN bytes (max 448, no inf,
+ *     0x7F/0xFF NaN).  bf16 and fp8 data are passed as raw bits.
+ *   - Alignment: every pointer 16-byte aligned; leading dimensions keep rows
+ *     16-byte aligned.
+ */
+#ifndef MOEFP8_H
+#define MOEFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)       /* null pointer, misalignment, bad enum, negative size   */
+#define MOE_ERR_UNSUPPORTED_SHAPE (-2) /* a size the kernels do not handle (e.g. not % 128)     */
+#define MOE_ERR_WORKSPACE (-3)         /* workspace missing or smaller than required            */
+#define MOE_ERR_HIP (-4)               /* a HIP launch failed (hipGetLastError after enqueue)   */
+
+/* ---- element types ---- */
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+#define MOE_DTYPE_U8 2
+
+/* ---- group score rule (the pages give none; see moe_route) ---- */
+#define MOE_GROUP_SCORE_TOP2_SUM 0     /* sum of the two largest biased scores of the group */
+#define MOE_GROUP_SCORE_MAX 1          /* largest biased score of the group                 */
+
+/* ---- flags ---- */
+#define MOE_ROUTE_SCORES_GIVEN 1       /* moe_route / moe_ffn_forward: `scores` is an input   */
+#define MOE_FWD_DETERMINISTIC 2        /* moe_ffn_forward: slot-ordered combine, no atomics   */
+
+/* ---- grouped GEMM epilogues ---- */
+#define MOE_EPI_STORE_F32 0            /* out f32 [M][N]                                        */
+#define MOE_EPI_STORE_BF16 1           /* out bf16 [M][N], round to nearest even                */
+#define MOE_EPI_SWIGLU_QUANT 2         /* N = 2W, B rows [gate; up]: out = e4m3 codes [M][W] of
+                                          h = silu(gate) * up, epi->h_s f32 [M][W/128]          */
+#define MOE_EPI_WEIGHTED_SCATTER_ADD 3 /* out f32 [R][N]: out[dst_row[m]] += row_weight[m] * y[m]
+                                          (fp32 atomics: bits vary run to run)                  */
+
+/* Layer configuration.  Field names follow the model config ([R1 card]). */
+typedef struct moe_cfg {
+  int hidden;        /* d_model; % 128 == 0                                              */
+  int inter;         /* routed expert width (moe_intermediate_size); % 128 == 0           */
+  int n_experts;     /* routed experts; 0 = a dense gated FFN (only the "shared" MLP)     */
+  int top_k;         /* experts per token (num_experts_per_tok)                            */
+  int n_shared;      /* 0 or 1 always-on gated MLP                                         */
+  int inter_shared;  /* its width; % 128 == 0                                              */
+  int n_group;       /* expert groups: contiguous id blocks of n_experts / n_group         */
+  int topk_group;    /* groups kept per token                                              */
+  int group_score;   /* MOE_GROUP_SCORE_*                                                  */
+  float routed_scale;/* multiplies the normalised routed weights (1.0)                     */
+} moe_cfg_t;
+
+/* Device pointers to one layer's weights.  Expert e's blocks start at
+ * e * (its matrix size); scales hold one fp32 per 128x128 block.           */
+typedef struct moe_weights {
+  const uint16_t* w_router; /* bf16 [E][hidden]                                     */
+  const float* bias;        /* f32 [E] routing-only bias, or NULL (= 0)             */
+  const uint8_t* w13_q;     /* e4m3 [E][2*inter][hidden], rows [gate; up]           */
+  const float* w13_s;       /* f32 [E][2*inter/128][hidden/128]                     */
+  const uint8_t* w2_q;      /* e4m3 [E][hidden][inter]                              */
+  const float* w2_s;        /* f32 [E][hidden/128][inter/128]                       */
+  const uint8_t* sh_w13_q;  /* shared expert / dense MLP: e4m3 [2*inter_shared][hidden] */
+  const float* sh_w13_s;    /* f32 [2*inter_shared/128][hidden/128]                 */
+  const uint8_t* sh_w2_q;   /* e4m3 [hidden][inter_shared]                          */
+  const float* sh_w2_s;     /* f32 [hidden/128][inter_shared/128]                   */
+} moe_weights_t;
+
+/* Extra epilogue operands of fp8_grouped_gemm_blockscaled. */
+typedef struct moe_epi {
+  float* h_s;                /* SWIGLU_QUANT: f32 [M][W/128] scales of the output codes      */
+  const int32_t* dst_row;    /* WEIGHTED_SCATTER_ADD: destination row of each logical row m */
+  const float* row_weight;   /* WEIGHTED_SCATTER_ADD: weight per row m, or NULL (= 1)       */
+} moe_epi_t;
+
+MOE_API const char* moe_status_string(int status);
+MOE_API const char* moe_last_error(void);
+
+/* fp8_quant_1x128 - online activation quantisation ([arch blog] "Fine granularity
+ * quantization", "Online Quantization").  Per row, per 128 consecutive columns:
+ * amax = max |v|; s = fp32(amax / 448) (correctly rounded; 1.0 for an all-zero
+ * tile); q = e4m3(fp32(v / s)) rounded to nearest even, saturating.
+ *   x      [rows][ld_x] of x_dtype (MOE_DTYPE_BF16 or MOE_DTYPE_F32), cols used
+ *   q      e4m3 [rows][ld_q]
+ *   s      f32 [rows][cols/128]
+ * cols % 128 == 0; ld_x >= cols, ld_q >= cols, rows >= 0 (0: no-op).          */
+MOE_API int fp8_quant_1x128(const void* x, int x_dtype, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
+                    void* stream);
+
+/* fp8_quant_128x128 - weight preparation (not on the timed path): the same rule
+ * over 128x128 blocks ([aguasto] "Quantization": blockwise FP8).
+ *   w f32 [rows][cols] -> q e4m3 [rows][cols], s f32 [rows/128][cols/128].   */
+MOE_API int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, void* stream);
+
+/* moe_route - gating ([arch blog] "Local Balanced Routing to Experts").
+ * Without MOE_ROUTE_SCORES_GIVEN: scores[t][e] = sigmoid(sum_d x[t][d] * w_router[e][d])
+ * (bf16 operands, fp32 accumulation) is computed and written.  With it, x and
+ * w_router are ignored and `scores` is read.  Then, in fp32:
+ *   b = scores + bias (bias only selects); groups of n_experts/n_group contiguous
+ *   experts are scored by cfg->group_score; the topk_group best groups are kept
+ *   (ties: lower group index); the top_k experts by b among them are chosen
+ *   (ties: lower expert index), slot j = j-th best;
+ *   topk_w[t][j] = fp32(scores[t][e_j] / S) * routed_scale, S = fp32 sum of the
+ *   chosen scores in slot order.
+ *   x bf16 [T][hidden] or NULL; w_router bf16 [E][hidden] or NULL; bias f32 [E] or NULL;
+ *   scores f32 [T][E] (in or out); topk_idx i32 [T][top_k]; topk_w f32 [T][top_k].
+ * Requires n_experts % n_group == 0, topk_group <= n_group, top_k <= topk_group *
+ * n_experts / n_group, n_experts <= 1024, n_group <= 64, top_k <= 64.          */
+MOE_API int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, const moe_cfg_t* cfg,
+              float* scores, int flags, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* moe_permute - sort the T*k assignments a = t*k + j by expert, stably (by
+ * expert, then a).  offsets[e]..offsets[e+1] is expert e's range of sorted
+ * rows; sorted_assign[p] = a at sorted position p; assign_pos[a] = p.
+ * Optionally gathers rows: rows_out[p] = rows_in[sorted_assign[p] / k]
+ * (row_bytes each, a multiple of 16; pass NULL for both to skip).
+ *   topk_idx i32 [T][k]; offsets i32 [E+1]; sorted_assign, assign_pos i32 [T*k].
+ * Scratch: the call needs moe_permute_workspace_size(T, k, E) bytes in `ws`. */
+MOE_API size_t moe_permute_workspace_size(int T, int k, int E);
+MOE_API int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* offsets, int32_t* sorted_assign,
+                int32_t* assign_pos, const void* rows_in, int row_bytes, void* rows_out, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* moe_unpermute - the inverse of moe_permute and the routed combine.
+ *   topk_w == NULL: out[t][j][:] = y_sorted[assign_pos[t*k+j]][:] (same dtype:
+ *     F32, BF16 or U8), so unpermute(permute(rows)) repeats each row k times.
+ *   topk_w != NULL (y_dtype F32): out bf16 [T][d] =
+ *     bf16(sum_j topk_w[t][j] * y_sorted[assign_pos[t*k+j]] + shared_y[t]),
+ *     summed in fp32 in slot order, shared_y f32 [T][d] or NULL (shared weight 1,
+ *     [arch blog] "Structural change").  d % 4 == 0.                          */
+MOE_API int moe_unpermute(const void* y_sorted, int y_dtype, const int32_t* assign_pos, const float* topk_w,
+                  const float* shared_y, int T, int k, int d, void* out, void* stream);
+
+/* fp8_grouped_gemm_blockscaled - C_g = A_g . B_g^T for each group g, with
+ * blockwise scales promoted into an fp32 accumulator once per 128-wide K block
+ * ([arch blog] "Fine granularity quantization", "Better Accumulation Precision"):
+ *   C[m][n] = sum_kb a_s[row(m)][kb] * b_s[g][n/128][kb] * sum_{k in kb} A[row(m)][k] B[g][n][k]
+ *   a_q e4m3 [*][K], a_s f32 [*][K/128]; row(m) = a_gather[m] or m if NULL;
+ *   b_q e4m3 [G][N][K], b_s f32 [G][N/128][K/128];
+ *   offsets i32 [G+1] (device): group g owns logical rows offsets[g]..offsets[g+1];
+ *   M_max: an upper bound of offsets[G] known on the host (sizes the launch).
+ *   epilogue MOE_EPI_* with `out` and `epi` as documented at the constants.
+ * N % 128 == 0 (SWIGLU_QUANT: N % 256 == 0), K % 128 == 0, G >= 1.  G = 1 with
+ * offsets {0, M} is a plain block-scaled GEMM (the dense layer).            */
+MOE_API int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int32_t* a_gather, const uint8_t* b_q,
+                                 const float* b_s, const int32_t* offsets, int G, int M_max, int N, int K,
+                                 int epilogue, const moe_epi_t* epi, void* out, void* stream);
+
+/* moe_ffn_workspace_size - bytes of device workspace moe_ffn_forward needs
+ * for T tokens (host-only; 0 on invalid arguments).                         */
+MOE_API size_t moe_ffn_workspace_size(int T, const moe_cfg_t* cfg);
+
+/* moe_ffn_forward - one MoE FFN layer ([R1 card], [arch blog] "More
+ * Aggressive Mixture-of-Expert", "Structural change"):
+ *   x -> 1x128 e4m3; scores, routing (moe_route); permutation (moe_permute);
+ *   per expert h = silu(x W_gate^T) * (x W_up^T) -> 1x128 e4m3; y = h W_down^T;
+ *   out[t] = bf16(sum_j topk_w[t][j] * y[t][j] + y_shared[t]).
+ * n_experts == 0 runs the dense gated FFN (x -> shared MLP -> out).
+ *   x bf16 [T][hidden]; out bf16 [T][hidden];
+ *   scores f32 [T][E], topk_idx i32 [T][k], topk_w f32 [T][k]: optional outputs
+ *   (NULL to skip); with MOE_ROUTE_SCORES_GIVEN `scores` is an input instead.
+ *   MOE_FWD_DETERMINISTIC: bit-reproducible combine (slot-ordered) instead of
+ *   fp32 atomics; it is also what the library does when T is small.
+ * ws: at least moe_ffn_workspace_size(T, cfg) bytes, 256-byte aligned.     */
+MOE_API int moe_ffn_forward(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
+                    size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w, int flags,
+                    void* stream);
+
+/* moe_ffn_forward_stages - moe_ffn_forward with hipEvent_t handles (passed as
+ * void*, created by the caller) recorded on `stream` between its stages, for
+ * live per-stage timing of the same launches:
+ *   events[0] before quantising x, [1] after it, [2] after routing and the
+ *   permutation, [3] after the gate/up GEMM, [4] after the down GEMM,
+ *   [5] after the combine/cast.
+ * n_events must be 0 (then it is moe_ffn_forward) or MOE_FWD_STAGE_EVENTS.  */
+#define MOE_FWD_STAGE_EVENTS 6
+MOE_API int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
+                                   size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w,
+                                   int flags, void* const* events, int n_events, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEFP8_H */

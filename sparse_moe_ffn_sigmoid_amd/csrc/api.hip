@@ -1,0 +1,477 @@
+// C ABI of libmoefp8: argument checks, workspace carve-up and kernel launches.
+// Every entry point validates on the host before enqueueing anything and
+// returns a status; launches are asynchronous on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+#include "moefp8.h"
+
+using namespace moefp8;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define HIP_TRY(expr, what)                       \
+  do {                                            \
+    const int st_ = hip_check((expr), (what));    \
+    if (st_ != MOE_OK) return st_;                \
+  } while (0)
+
+// Routing configuration checks shared by moe_route and moe_ffn_forward.
+int check_route_cfg(const moe_cfg_t* c) {
+  REQUIRE(c, MOE_ERR_INVALID_ARG, "cfg is NULL");
+  REQUIRE(c->n_experts >= 1 && c->n_experts <= 1024, MOE_ERR_UNSUPPORTED_SHAPE, "n_experts %d not in [1, 1024]",
+          c->n_experts);
+  REQUIRE(c->n_group >= 1 && c->n_group <= 64, MOE_ERR_UNSUPPORTED_SHAPE, "n_group %d not in [1, 64]", c->n_group);
+  REQUIRE(c->n_experts % c->n_group == 0, MOE_ERR_UNSUPPORTED_SHAPE, "n_experts %d %% n_group %d != 0", c->n_experts,
+          c->n_group);
+  REQUIRE(c->topk_group >= 1 && c->topk_group <= c->n_group, MOE_ERR_INVALID_ARG, "topk_group %d not in [1, %d]",
+          c->topk_group, c->n_group);
+  const int pool = c->topk_group * (c->n_experts / c->n_group);
+  REQUIRE(c->top_k >= 1 && c->top_k <= pool && c->top_k <= 64, MOE_ERR_INVALID_ARG,
+          "top_k %d not in [1, min(64, topk_group * n_experts / n_group = %d)]", c->top_k, pool);
+  REQUIRE(c->group_score == MOE_GROUP_SCORE_TOP2_SUM || c->group_score == MOE_GROUP_SCORE_MAX, MOE_ERR_INVALID_ARG,
+          "group_score %d unknown", c->group_score);
+  return MOE_OK;
+}
+
+int check_layer_cfg(const moe_cfg_t* c) {
+  REQUIRE(c, MOE_ERR_INVALID_ARG, "cfg is NULL");
+  REQUIRE(c->hidden > 0 && c->hidden % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d not a positive multiple of 128",
+          c->hidden);
+  REQUIRE(c->n_shared == 0 || c->n_shared == 1, MOE_ERR_UNSUPPORTED_SHAPE, "n_shared %d not 0 or 1", c->n_shared);
+  if (c->n_shared) {
+    REQUIRE(c->inter_shared > 0 && c->inter_shared % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE,
+            "inter_shared %d not a positive multiple of 128", c->inter_shared);
+  }
+  if (c->n_experts == 0) {
+    REQUIRE(c->n_shared == 1, MOE_ERR_INVALID_ARG, "a dense layer (n_experts = 0) needs n_shared = 1");
+    return MOE_OK;
+  }
+  const int st = check_route_cfg(c);
+  if (st != MOE_OK) return st;
+  REQUIRE(c->inter > 0 && c->inter % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "inter %d not a positive multiple of 128",
+          c->inter);
+  REQUIRE(c->n_experts % 16 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "n_experts %d not a multiple of 16 (router tiles)",
+          c->n_experts);
+  return MOE_OK;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Workspace layout of moe_ffn_forward (offsets from ws, 256-byte aligned).
+struct FwdLayout {
+  size_t x_q, x_s, scores, topk_idx, topk_w, offsets, sorted_assign, assign_pos, sorted_token, sorted_w, perm_scratch,
+      h_q, h_s, hs_q, hs_s, y_sorted, y_shared, total;
+};
+
+FwdLayout fwd_layout(int T, const moe_cfg_t* c) {
+  FwdLayout L{};
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p += align_up(bytes);
+    return at;
+  };
+  const size_t t = (size_t)T, d = (size_t)c->hidden;
+  const size_t E = (size_t)c->n_experts, k = (size_t)(c->n_experts ? c->top_k : 0);
+  const size_t n = t * k;
+  L.x_q = take(t * d);
+  L.x_s = take(t * (d / 128) * 4);
+  L.scores = take(t * E * 4);
+  L.topk_idx = take(n * 4);
+  L.topk_w = take(n * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted_assign = take(n * 4);
+  L.assign_pos = take(n * 4);
+  L.sorted_token = take(n * 4);
+  L.sorted_w = take(n * 4);
+  L.perm_scratch = take(E ? permute_scratch_bytes((int)n, (int)E) : 0);
+  const size_t w = E ? (size_t)c->inter : 0, ws = c->n_shared ? (size_t)c->inter_shared : 0;
+  L.h_q = take(n * w);
+  L.h_s = take(n * (w / 128) * 4);
+  L.hs_q = take(t * ws);
+  L.hs_s = take(t * (ws / 128) * 4);
+  L.y_sorted = take(n * d * 4);
+  L.y_shared = take(t * d * 4);
+  L.total = p;
+  return L;
+}
+
+// Assignments at or above this count combine with fp32 atomics unless the
+// caller asks for the deterministic slot-ordered combine.
+constexpr long kAtomicCombineMin = 8192;
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int fp8_quant_1x128(const void* x, int x_dtype, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
+                    void* stream) {
+  REQUIRE(x_dtype == MOE_DTYPE_BF16 || x_dtype == MOE_DTYPE_F32, MOE_ERR_INVALID_ARG, "x_dtype %d not BF16/F32",
+          x_dtype);
+  REQUIRE(rows >= 0, MOE_ERR_INVALID_ARG, "rows %d < 0", rows);
+  REQUIRE(cols > 0 && cols % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "cols %d not a positive multiple of 128", cols);
+  REQUIRE(ld_x >= cols && ld_q >= cols, MOE_ERR_INVALID_ARG, "ld_x %d / ld_q %d smaller than cols %d", ld_x, ld_q,
+          cols);
+  if (rows == 0) return ok();
+  REQUIRE(x && q && s, MOE_ERR_INVALID_ARG, "NULL pointer");
+  const int esz = x_dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  REQUIRE(aligned(x, 16) && ((size_t)ld_x * esz) % 16 == 0, MOE_ERR_INVALID_ARG, "x rows not 16-byte aligned");
+  REQUIRE(aligned(q, 16) && ld_q % 16 == 0 && aligned(s, 4), MOE_ERR_INVALID_ARG, "q/s not aligned");
+  HIP_TRY(launch_quant_1x128(x, x_dtype == MOE_DTYPE_BF16, rows, cols, ld_x, q, ld_q, s, (hipStream_t)stream),
+          "fp8_quant_1x128");
+  return ok();
+}
+
+int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, void* stream) {
+  REQUIRE(rows >= 0 && cols >= 0, MOE_ERR_INVALID_ARG, "negative size");
+  REQUIRE(rows % 128 == 0 && cols % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "rows %d / cols %d not multiples of 128",
+          rows, cols);
+  if (rows == 0 || cols == 0) return ok();
+  REQUIRE(w && q && s, MOE_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(s, 4), MOE_ERR_INVALID_ARG, "pointer not aligned");
+  HIP_TRY(launch_quant_128x128(w, rows, cols, q, s, (hipStream_t)stream), "fp8_quant_128x128");
+  return ok();
+}
+
+int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, const moe_cfg_t* cfg,
+              float* scores, int flags, int32_t* topk_idx, float* topk_w, void* stream) {
+  int st = check_route_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T %d < 0", T);
+  REQUIRE((flags & ~MOE_ROUTE_SCORES_GIVEN) == 0, MOE_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (T == 0) return ok();
+  REQUIRE(scores && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "NULL scores/topk_idx/topk_w");
+  const hipStream_t s = (hipStream_t)stream;
+  if (!(flags & MOE_ROUTE_SCORES_GIVEN)) {
+    REQUIRE(x && w_router, MOE_ERR_INVALID_ARG, "x and w_router are needed unless MOE_ROUTE_SCORES_GIVEN");
+    REQUIRE(cfg->hidden > 0 && cfg->hidden % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d not a multiple of 128",
+            cfg->hidden);
+    REQUIRE(cfg->n_experts % 16 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "n_experts %d not a multiple of 16", cfg->n_experts);
+    REQUIRE(aligned(x, 16) && aligned(w_router, 16), MOE_ERR_INVALID_ARG, "x / w_router not 16-byte aligned");
+    HIP_TRY(launch_router(x, w_router, T, cfg->n_experts, cfg->hidden, scores, s), "router");
+  }
+  HIP_TRY(launch_route(scores, bias, T, cfg->n_experts, cfg->top_k, cfg->n_group, cfg->topk_group, cfg->group_score,
+                       cfg->routed_scale, topk_idx, topk_w, s),
+          "moe_route");
+  return ok();
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1 || E > 1024 || (long)T * k > (1l << 30)) return 0;
+  return align_up(permute_scratch_bytes(T * k, E));
+}
+
+int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* offsets, int32_t* sorted_assign,
+                int32_t* assign_pos, const void* rows_in, int row_bytes, void* rows_out, void* ws, size_t ws_bytes,
+                void* stream) {
+  REQUIRE(T >= 0 && k >= 1 && E >= 1, MOE_ERR_INVALID_ARG, "T %d, k %d, E %d", T, k, E);
+  REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED_SHAPE, "E %d > 1024", E);
+  REQUIRE((long)T * k <= (1l << 30), MOE_ERR_UNSUPPORTED_SHAPE, "T*k too large");
+  REQUIRE(offsets, MOE_ERR_INVALID_ARG, "offsets is NULL");
+  REQUIRE((rows_in == nullptr) == (rows_out == nullptr), MOE_ERR_INVALID_ARG, "rows_in/rows_out: both or neither");
+  if (rows_in) {
+    REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, MOE_ERR_INVALID_ARG, "row_bytes %d not a positive multiple of 16",
+            row_bytes);
+    REQUIRE(aligned(rows_in, 16) && aligned(rows_out, 16), MOE_ERR_INVALID_ARG, "rows not 16-byte aligned");
+  }
+  if (T > 0) REQUIRE(topk_idx && sorted_assign && assign_pos, MOE_ERR_INVALID_ARG, "NULL pointer");
+  const size_t need = moe_permute_workspace_size(T, k, E);
+  REQUIRE(need == 0 || (ws && ws_bytes >= need), MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(launch_permute(topk_idx, T, k, E, offsets, sorted_assign, assign_pos, nullptr, nullptr, nullptr,
+                         reinterpret_cast<int32_t*>(ws), s),
+          "moe_permute");
+  if (rows_in) HIP_TRY(launch_gather_rows(rows_in, row_bytes, T * k, k, sorted_assign, rows_out, s), "gather rows");
+  return ok();
+}
+
+int moe_unpermute(const void* y_sorted, int y_dtype, const int32_t* assign_pos, const float* topk_w,
+                  const float* shared_y, int T, int k, int d, void* out, void* stream) {
+  REQUIRE(T >= 0 && k >= 1 && d >= 1, MOE_ERR_INVALID_ARG, "T %d, k %d, d %d", T, k, d);
+  REQUIRE(y_dtype == MOE_DTYPE_F32 || y_dtype == MOE_DTYPE_BF16 || y_dtype == MOE_DTYPE_U8, MOE_ERR_INVALID_ARG,
+          "y_dtype %d unknown", y_dtype);
+  REQUIRE(d % 4 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "d %d not a multiple of 4", d);
+  if (T == 0) return ok();
+  REQUIRE(y_sorted && assign_pos && out, MOE_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned(y_sorted, 16) && aligned(out, 16) && (!shared_y || aligned(shared_y, 16)), MOE_ERR_INVALID_ARG,
+          "pointer not 16-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  if (topk_w) {
+    REQUIRE(y_dtype == MOE_DTYPE_F32, MOE_ERR_INVALID_ARG, "the weighted combine takes F32 rows");
+    HIP_TRY(launch_combine(reinterpret_cast<const float*>(y_sorted), assign_pos, topk_w, shared_y, T, k, d,
+                           reinterpret_cast<uint16_t*>(out), s),
+            "moe_unpermute (combine)");
+  } else {
+    const int esz = y_dtype == MOE_DTYPE_F32 ? 4 : (y_dtype == MOE_DTYPE_BF16 ? 2 : 1);
+    HIP_TRY(launch_unpermute(y_sorted, assign_pos, (long)T * k, d * esz, out, s), "moe_unpermute");
+  }
+  return ok();
+}
+
+int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int32_t* a_gather, const uint8_t* b_q,
+                                 const float* b_s, const int32_t* offsets, int G, int M_max, int N, int K, int epilogue,
+                                 const moe_epi_t* epi, void* out, void* stream) {
+  REQUIRE(G >= 1 && G <= 1024, MOE_ERR_UNSUPPORTED_SHAPE, "G %d not in [1, 1024]", G);
+  REQUIRE(M_max >= 0 && N > 0 && K > 0, MOE_ERR_INVALID_ARG, "M_max %d, N %d, K %d", M_max, N, K);
+  REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "N %d / K %d not multiples of 128", N, K);
+  REQUIRE(epilogue >= MOE_EPI_STORE_F32 && epilogue <= MOE_EPI_WEIGHTED_SCATTER_ADD, MOE_ERR_INVALID_ARG,
+          "epilogue %d unknown", epilogue);
+  if (epilogue == MOE_EPI_SWIGLU_QUANT)
+    REQUIRE(N % 256 == 0 && epi && epi->h_s, MOE_ERR_INVALID_ARG, "SWIGLU_QUANT needs N %% 256 == 0 and epi->h_s");
+  if (M_max == 0) return ok();
+  REQUIRE(a_q && a_s && b_q && b_s && offsets && out, MOE_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned(a_q, 16) && aligned(b_q, 16) && aligned(out, 16), MOE_ERR_INVALID_ARG, "pointer not 16-byte aligned");
+  GemmArgs args{};
+  GemmSeg& sg = args.seg[1];
+  const int bm = gemm_pick_bm(M_max, G);
+  sg.a_q = a_q;
+  sg.a_s = a_s;
+  sg.a_gather = a_gather;
+  sg.b_q = b_q;
+  sg.b_s = b_s;
+  sg.b_stride = (long long)N * K;
+  sg.bs_stride = (long long)(N / 128) * (K / 128);
+  sg.offsets = offsets;
+  sg.G = G;
+  sg.m_tiles = (int)(((long)M_max + (long)G * (bm - 1)) / bm);
+  sg.N = N;
+  sg.K = K;
+  sg.out = out;
+  if (epilogue == MOE_EPI_SWIGLU_QUANT) {
+    sg.out_s = epi->h_s;
+    sg.ld_out = N / 2;
+  } else {
+    sg.ld_out = N;
+  }
+  if (epilogue == MOE_EPI_WEIGHTED_SCATTER_ADD && epi) {
+    sg.dst_row = epi->dst_row;
+    sg.row_w = epi->row_weight;
+  }
+  static const int kEpiMap[4] = {kEpiF32, kEpiBf16, kEpiSwiglu, kEpiScatter};
+  HIP_TRY(launch_grouped_gemm(args, kEpiMap[epilogue], bm, (hipStream_t)stream), "fp8_grouped_gemm_blockscaled");
+  return ok();
+}
+
+size_t moe_ffn_workspace_size(int T, const moe_cfg_t* cfg) {
+  if (T < 0 || check_layer_cfg(cfg) != MOE_OK) return 0;
+  return fwd_layout(T, cfg).total;
+}
+
+int moe_ffn_forward(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
+                    size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w, int flags,
+                    void* stream) {
+  return moe_ffn_forward_stages(x, T, cfg, w, ws, ws_bytes, out, scores, topk_idx, topk_w, flags, nullptr, 0, stream);
+}
+
+int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
+                           size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w, int flags,
+                           void* const* events, int n_events, void* stream) {
+  int st = check_layer_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T %d < 0", T);
+  REQUIRE((flags & ~(MOE_ROUTE_SCORES_GIVEN | MOE_FWD_DETERMINISTIC)) == 0, MOE_ERR_INVALID_ARG, "unknown flags 0x%x",
+          flags);
+  REQUIRE((long)T * (cfg->n_experts ? cfg->top_k : 1) <= (1l << 30), MOE_ERR_UNSUPPORTED_SHAPE, "T too large");
+  REQUIRE(n_events == 0 || (events && n_events == MOE_FWD_STAGE_EVENTS), MOE_ERR_INVALID_ARG,
+          "n_events %d (0 or %d)", n_events, MOE_FWD_STAGE_EVENTS);
+  for (int i = 0; i < n_events; ++i) REQUIRE(events[i], MOE_ERR_INVALID_ARG, "event %d is NULL", i);
+  if (T == 0) return ok();
+  REQUIRE(x && out && w, MOE_ERR_INVALID_ARG, "NULL x / out / weights");
+  REQUIRE(aligned(x, 16) && aligned(out, 16), MOE_ERR_INVALID_ARG, "x / out not 16-byte aligned");
+  const bool routed = cfg->n_experts > 0;
+  if (routed) {
+    REQUIRE(w->w13_q && w->w13_s && w->w2_q && w->w2_s, MOE_ERR_INVALID_ARG, "NULL routed expert weights");
+    if (flags & MOE_ROUTE_SCORES_GIVEN)
+      REQUIRE(scores, MOE_ERR_INVALID_ARG, "MOE_ROUTE_SCORES_GIVEN needs scores");
+    else
+      REQUIRE(w->w_router, MOE_ERR_INVALID_ARG, "NULL router weights");
+  }
+  if (cfg->n_shared)
+    REQUIRE(w->sh_w13_q && w->sh_w13_s && w->sh_w2_q && w->sh_w2_s, MOE_ERR_INVALID_ARG, "NULL shared weights");
+  const FwdLayout L = fwd_layout(T, cfg);
+  REQUIRE(ws && aligned(ws, 256) && ws_bytes >= L.total, MOE_ERR_WORKSPACE,
+          "workspace %zu bytes (needs %zu, 256-byte aligned)", ws_bytes, L.total);
+
+  const hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int i) -> hipError_t {
+    return n_events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+  };
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  auto at = [&](size_t off) { return base + off; };
+  const int d = cfg->hidden, E = cfg->n_experts, k = routed ? cfg->top_k : 0;
+  const int W = cfg->inter, Ws = cfg->inter_shared;
+  uint8_t* x_q = at(L.x_q);
+  float* x_s = reinterpret_cast<float*>(at(L.x_s));
+  HIP_TRY(mark(0), "event");
+  HIP_TRY(launch_quant_1x128(x, true, T, d, d, x_q, d, x_s, s), "quantize x");
+  HIP_TRY(mark(1), "event");
+
+  int32_t* sorted_token = reinterpret_cast<int32_t*>(at(L.sorted_token));
+  int32_t* assign_pos = reinterpret_cast<int32_t*>(at(L.assign_pos));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(L.offsets));
+  float* sorted_w = reinterpret_cast<float*>(at(L.sorted_w));
+  float* tw = topk_w ? topk_w : reinterpret_cast<float*>(at(L.topk_w));
+  const long n_assign = (long)T * k;
+  const bool atomic_combine = routed && !(flags & MOE_FWD_DETERMINISTIC) && n_assign >= kAtomicCombineMin;
+  if (routed) {
+    float* sc = scores ? scores : reinterpret_cast<float*>(at(L.scores));
+    int32_t* ti = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(L.topk_idx));
+    if (!(flags & MOE_ROUTE_SCORES_GIVEN)) HIP_TRY(launch_router(x, w->w_router, T, E, d, sc, s), "router");
+    HIP_TRY(launch_route(sc, w->bias, T, E, k, cfg->n_group, cfg->topk_group, cfg->group_score, cfg->routed_scale, ti,
+                         tw, s),
+            "route");
+    HIP_TRY(launch_permute(ti, T, k, E, offsets, reinterpret_cast<int32_t*>(at(L.sorted_assign)), assign_pos,
+                           sorted_token, atomic_combine ? tw : nullptr, atomic_combine ? sorted_w : nullptr,
+                           reinterpret_cast<int32_t*>(at(L.perm_scratch)), s),
+            "permute");
+  }
+  HIP_TRY(mark(2), "event");
+
+  // gate/up GEMM with the SwiGLU + 1x128 requantisation epilogue
+  uint8_t* h_q = at(L.h_q);
+  float* h_s = reinterpret_cast<float*>(at(L.h_s));
+  uint8_t* hs_q = at(L.hs_q);
+  float* hs_s = reinterpret_cast<float*>(at(L.hs_s));
+  const int bm = routed ? gemm_pick_bm(n_assign, E) : gemm_pick_bm(T, 1);
+  GemmArgs up{};
+  if (cfg->n_shared) {
+    GemmSeg& g0 = up.seg[0];
+    g0.a_q = x_q;
+    g0.a_s = x_s;
+    g0.b_q = w->sh_w13_q;
+    g0.b_s = w->sh_w13_s;
+    g0.G = 1;
+    g0.m_rows = T;
+    g0.m_tiles = (T + bm - 1) / bm;
+    g0.N = 2 * Ws;
+    g0.K = d;
+    g0.out = hs_q;
+    g0.out_s = hs_s;
+    g0.ld_out = Ws;
+  }
+  if (routed) {
+    GemmSeg& g1 = up.seg[1];
+    g1.a_q = x_q;
+    g1.a_s = x_s;
+    g1.a_gather = sorted_token;
+    g1.b_q = w->w13_q;
+    g1.b_s = w->w13_s;
+    g1.b_stride = (long long)2 * W * d;
+    g1.bs_stride = (long long)(2 * W / 128) * (d / 128);
+    g1.offsets = offsets;
+    g1.G = E;
+    g1.m_tiles = (int)((n_assign + (long)E * (bm - 1)) / bm);
+    g1.N = 2 * W;
+    g1.K = d;
+    g1.out = h_q;
+    g1.out_s = h_s;
+    g1.ld_out = W;
+  }
+  HIP_TRY(launch_grouped_gemm(up, kEpiSwiglu, bm, s), "gate/up GEMM");
+  HIP_TRY(mark(3), "event");
+
+  // down GEMM: routed rows in sorted order, then the combine
+  float* y_sorted = reinterpret_cast<float*>(at(L.y_sorted));
+  float* y_shared = reinterpret_cast<float*>(at(L.y_shared));
+  GemmArgs dn{};
+  int epi = kEpiF32;
+  if (!routed) {
+    epi = kEpiBf16;                            // dense layer: the shared MLP writes the output directly
+  } else if (atomic_combine) {
+    epi = kEpiScatter;
+    HIP_TRY(launch_fill_zero(y_shared, (long)T * d, s), "zero accumulator");
+  }
+  if (cfg->n_shared) {
+    GemmSeg& g0 = dn.seg[0];
+    g0.a_q = hs_q;
+    g0.a_s = hs_s;
+    g0.b_q = w->sh_w2_q;
+    g0.b_s = w->sh_w2_s;
+    g0.G = 1;
+    g0.m_rows = T;
+    g0.m_tiles = (T + bm - 1) / bm;
+    g0.N = d;
+    g0.K = Ws;
+    g0.out = routed ? (void*)y_shared : (void*)out;
+    g0.ld_out = d;
+  }
+  if (routed) {
+    GemmSeg& g1 = dn.seg[1];
+    g1.a_q = h_q;
+    g1.a_s = h_s;
+    g1.b_q = w->w2_q;
+    g1.b_s = w->w2_s;
+    g1.b_stride = (long long)d * W;
+    g1.bs_stride = (long long)(d / 128) * (W / 128);
+    g1.offsets = offsets;
+    g1.G = E;
+    g1.m_tiles = (int)((n_assign + (long)E * (bm - 1)) / bm);
+    g1.N = d;
+    g1.K = W;
+    g1.out = atomic_combine ? (void*)y_shared : (void*)y_sorted;
+    g1.ld_out = d;
+    if (atomic_combine) {
+      g1.dst_row = sorted_token;
+      g1.row_w = sorted_w;
+    }
+  }
+  HIP_TRY(launch_grouped_gemm(dn, epi, bm, s), "down GEMM");
+  HIP_TRY(mark(4), "event");
+  if (routed) {
+    if (atomic_combine) {
+      HIP_TRY(launch_cast_bf16(y_shared, (long)T * d, out, s), "cast");
+    } else {
+      HIP_TRY(launch_combine(y_sorted, assign_pos, tw, cfg->n_shared ? y_shared : nullptr, T, k, d, out, s),
+              "combine");
+    }
+  }
+  HIP_TRY(mark(5), "event");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Device helpers shared by the gfx950 kernels of libmoefp8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moefp8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16 bytes in registers
+
+constexpr int kWave = 64;
+
+// OCP E4M3FN encode of an fp32 value: round to nearest, ties to even mantissa,
+// sign kept, saturating at 448 (0x7E); NaN -> 0x7F.  Written from the format
+// definition: in the normal range (|f| >= 2^-6) the 23-bit fp32 fraction is
+// rounded to 3 bits by adding half an ulp minus one plus the kept lsb (round
+// half to even on the integer pattern) and the exponent is re-biased from 127
+// to 7; below 2^-6 the grid is the subnormal step 2^-9.
+__device__ __forceinline__ uint32_t e4m3_encode(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x7F800000u) {
+    code = 0x7Fu;                                   // NaN
+  } else if (a >= 0x43E00000u) {
+    code = 0x7Eu;                                   // >= 448 (and inf): saturate
+  } else if (a >= 0x3C800000u) {                    // >= 2^-6: normal
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // (exp32 << 3 | m3), carry included
+    code = r - (120u << 3);                         // exponent bias 127 -> 7
+    code = code > 0x7Eu ? 0x7Eu : code;
+  } else {
+    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);          // multiples of 2^-9, 0..8
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
+
+// silu(z) * u in fp32: z / (1 + e^-z) * u.
+__device__ __forceinline__ float swiglu(float z, float u) { return z / (1.0f + __expf(-z)) * u; }
+
+}  // namespace moefp8

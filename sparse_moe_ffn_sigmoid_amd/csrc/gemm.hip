@@ -1,0 +1,343 @@
+// Block-scaled FP8 grouped GEMM for gfx950 (onlylabs "DeepSeek v3 and R1 Model
+// Architecture", headings "Fine granularity quantization" and "Better
+// Accumulation Precision"; aguasto "DeepSeek-R1", "Quantization").
+//
+//   C[m][n] = sum_kb a_s[row(m)][kb] * b_s[g][n/128][kb] * (sum_{k in kb} A[row(m)][k] * B[g][n][k])
+//
+// One 128-wide K block is exactly one V_MFMA_F32_16X16X128_F8F6F4 (e4m3 x
+// e4m3 -> fp32) per 16x16 output tile.  Each block's partial is promoted into
+// the fp32 accumulator with one FMA per element: acc = fma(part, sa * sb, acc).
+//
+// Workgroup: 4 waves, BM rows x (128 * NB) B rows.  Every wave covers all BM
+// rows and 32 of each 128-row B block, so with NB = 2 (the gate/up GEMM, B rows
+// [gate block; up block]) a lane holds gate and up values of the same (row,
+// column) and SwiGLU is lane-local.  A and B tiles of one K block are staged
+// in LDS (16-byte chunks, XOR-swizzled by row so a 16-row fragment read is
+// bank-conflict free), double-buffered: the next block's global loads are in
+// flight while the current one feeds the MFMAs.
+//
+// Grouped rows: a static segment (the shared expert, or a plain GEMM) takes the
+// first m tiles of the grid; a dynamic segment (routed experts) takes the rest,
+// and each workgroup finds its (group, tile) from the device-side offsets with
+// an in-LDS prefix sum over the groups' tile counts.  Tiles past the real
+// count exit at once, so no device-to-host copy of the counts is needed.
+#include "common.h"
+#include "launch.h"
+
+namespace moefp8 {
+
+__device__ __forceinline__ int swz(int r, int c) { return (r << 7) + ((c ^ (r & 7)) << 4); }
+
+template <int BM, int NB>
+struct Tile {
+  static constexpr int kA = BM * 128;            // A codes of one K block
+  static constexpr int kB = NB * 128 * 128;      // B codes of one K block
+  static constexpr int kSA = BM * 4;             // a_s of the BM rows
+  static constexpr int kSB = 16;                 // b_s of the NB blocks
+  static constexpr int kStage = kA + kB + kSA + kSB;
+};
+
+template <int BM, int NB, int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) {
+  using TL = Tile<BM, NB>;
+  constexpr int MT = BM / 16;                 // 16-row tiles per wave
+  constexpr int NT = 2 * NB;                  // 16-col tiles per wave
+  constexpr int BN = 128 * NB;
+  constexpr int A_CH = BM * 8;                // 16-byte chunks per K block
+  constexpr int A_PER = (A_CH + 255) / 256;
+  constexpr int B_PER = BN * 8 / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::kStage];
+  __shared__ int scan_tmp[256];
+  __shared__ int pre[1024];
+  __shared__ int pick[1];
+  __shared__ float red[4][BM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
+  int v = blockIdx.x;
+  const int nt = blockIdx.y;
+  int si, g, m0, m_end;
+  if (v < args.seg[0].m_tiles) {
+    si = 0;
+    g = 0;
+    m0 = v * BM;
+    m_end = args.seg[0].m_rows;
+  } else {
+    v -= args.seg[0].m_tiles;
+    const GemmSeg& sd = args.seg[1];
+    if (v >= sd.m_tiles) return;
+    const int G = sd.G;
+    const int per = (G + 255) >> 8;           // groups per thread (G <= 1024)
+    int cnt[4];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gi = tid * per + i;
+      cnt[i] = 0;
+      if (i < per && gi < G) cnt[i] = (sd.offsets[gi + 1] - sd.offsets[gi] + BM - 1) / BM;
+      local += cnt[i];
+    }
+    scan_tmp[tid] = local;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int add = tid >= o ? scan_tmp[tid - o] : 0;
+      __syncthreads();
+      scan_tmp[tid] += add;
+      __syncthreads();
+    }
+    int run = scan_tmp[tid] - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gi = tid * per + i;
+      run += cnt[i];
+      if (i < per && gi < G) pre[gi] = run;   // inclusive prefix
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int lo = 0, hi = G;                       // first group with pre[g] > v
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] > v) hi = mid; else lo = mid + 1;
+      }
+      pick[0] = lo;
+    }
+    __syncthreads();
+    g = pick[0];
+    if (g >= G) return;                         // past the real tile count
+    si = 1;
+    const int tiles_g = (sd.offsets[g + 1] - sd.offsets[g] + BM - 1) / BM;
+    m0 = sd.offsets[g] + (v - (pre[g] - tiles_g)) * BM;
+    m_end = sd.offsets[g + 1];
+  }
+  // this tile's segment, field by field (kept in scalar registers)
+  const GemmSeg& s0 = args.seg[0];
+  const GemmSeg& s1 = args.seg[1];
+  const int K = si ? s1.K : s0.K, nkb = K >> 7;
+  const uint8_t* const a_q = si ? s1.a_q : s0.a_q;
+  const float* const a_s = si ? s1.a_s : s0.a_s;
+  const int32_t* const gat = si ? s1.a_gather : s0.a_gather;
+  const int half = (si ? s1.N : s0.N) / NB;     // B rows per block (N for NB = 1, W for SwiGLU)
+  if (nt * 128 >= half) return;
+  const uint8_t* const bq = (si ? s1.b_q : s0.b_q) + (long long)g * (si ? s1.b_stride : s0.b_stride);
+  const float* const bs = (si ? s1.b_s : s0.b_s) + (long long)g * (si ? s1.bs_stride : s0.bs_stride);
+
+  // per-thread global sources of the 16-byte chunks it stages each K block
+  const uint8_t* a_src[A_PER];
+  int a_dst[A_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    const int ci = tid + 256 * i;
+    const int r = (ci >> 3) < BM ? (ci >> 3) : 0;
+    const int m = m0 + r < m_end ? m0 + r : m0;
+    const long src = gat ? (long)gat[m] : (long)m;
+    a_src[i] = a_q + src * K + ((ci & 7) << 4);
+    a_dst[i] = swz(r, ci & 7);
+  }
+  const uint8_t* b_src[B_PER];
+  int b_dst[B_PER];
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) {
+    const int ci = tid + 256 * i;
+    const int rb = ci >> 3;
+    const int brow = (rb >> 7) * half + nt * 128 + (rb & 127);
+    b_src[i] = bq + (long)brow * K + ((ci & 7) << 4);
+    b_dst[i] = TL::kA + swz(rb, ci & 7);
+  }
+  // thread tid < BM stages a_s of row tid; threads BM .. BM+NB-1 stage b_s of block tid-BM
+  const float* s_src = nullptr;
+  int s_dst = 0;
+  if (tid < BM) {
+    const int m = m0 + tid < m_end ? m0 + tid : m0;
+    const long src = gat ? (long)gat[m] : (long)m;
+    s_src = a_s + src * nkb;
+    s_dst = TL::kA + TL::kB + tid * 4;
+  } else if (tid < BM + NB) {
+    s_src = bs + (long)((((tid - BM) * half) + nt * 128) >> 7) * nkb;
+    s_dst = TL::kA + TL::kB + TL::kSA + (tid - BM) * 4;
+  }
+
+  u32x4 ra[A_PER], rb[B_PER];
+  float rs = 0.0f;
+#define GEMM_GLOAD(kb_)                                                                      \
+  {                                                                                          \
+    const int ko_ = (kb_) << 7;                                                              \
+    _Pragma("unroll") for (int i = 0; i < A_PER; ++i) ra[i] =                               \
+        *reinterpret_cast<const u32x4*>(a_src[i] + ko_);                                     \
+    _Pragma("unroll") for (int i = 0; i < B_PER; ++i) rb[i] =                               \
+        *reinterpret_cast<const u32x4*>(b_src[i] + ko_);                                     \
+    if (s_src) rs = s_src[kb_];                                                              \
+  }
+#define GEMM_SSTORE(buf_)                                                                    \
+  {                                                                                          \
+    uint8_t* st_ = smem + (buf_) * TL::kStage;                                               \
+    _Pragma("unroll") for (int i = 0; i < A_PER; ++i) if ((tid + 256 * i) < A_CH)           \
+        *reinterpret_cast<u32x4*>(st_ + a_dst[i]) = ra[i];                                   \
+    _Pragma("unroll") for (int i = 0; i < B_PER; ++i)                                       \
+        *reinterpret_cast<u32x4*>(st_ + b_dst[i]) = rb[i];                                   \
+    if (s_src) *reinterpret_cast<float*>(st_ + s_dst) = rs;                                  \
+  }
+
+  v4f acc[MT][NT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NT; ++nj) acc[mi][nj] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  GEMM_GLOAD(0);
+  GEMM_SSTORE(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nkb) GEMM_GLOAD(kb + 1);
+    const uint8_t* st = smem + cur * TL::kStage;
+    v8i af[MT], bf[NT];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      const int r = mi * 16 + r16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + swz(r, q));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + swz(r, q + 4));
+      af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int nj = 0; nj < NT; ++nj) {
+      const int r = (nj >> 1) * 128 + wave * 32 + (nj & 1) * 16 + r16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + TL::kA + swz(r, q));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + TL::kA + swz(r, q + 4));
+      bf[nj] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    const float* sa = reinterpret_cast<const float*>(st + TL::kA + TL::kB);
+    const float* sb = reinterpret_cast<const float*>(st + TL::kA + TL::kB + TL::kSA);
+    v4f part[MT][NT];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < NT; ++nj)
+        part[mi][nj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[nj], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      const float4 s4 = *reinterpret_cast<const float4*>(sa + mi * 16 + 4 * q);
+      const float sav[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float sbv = sb[nb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float scl = sav[i] * sbv;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[mi][2 * nb + j][i] = fmaf(part[mi][2 * nb + j][i], scl, acc[mi][2 * nb + j][i]);
+        }
+      }
+    }
+    if (kb + 1 < nkb) GEMM_SSTORE(cur ^ 1);
+    __syncthreads();
+  }
+
+#undef GEMM_GLOAD
+#undef GEMM_SSTORE
+  // ---- epilogues: lane holds rows m0 + mi*16 + 4q + i, column wave*32 + j*16 + r16 of each B block ----
+  void* const out = si ? s1.out : s0.out;
+  float* const out_s = si ? s1.out_s : s0.out_s;
+  const int ld_out = si ? s1.ld_out : s0.ld_out;
+  const int32_t* const dst_row = si ? s1.dst_row : s0.dst_row;
+  const float* const row_w = si ? s1.row_w : s0.row_w;
+  if constexpr (EPI == kEpiSwiglu) {
+    float h[MT][2][4];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][2 + j][i]);
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = fmaxf(fabsf(h[mi][0][i]), fabsf(h[mi][1][i]));
+        mx = group_max<16>(mx);
+        if (r16 == 0) red[wave][mi * 16 + 4 * q + i] = mx;
+      }
+    __syncthreads();
+    uint8_t* stage = smem;                        // BM x 128 codes, row-major
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mi * 16 + 4 * q + i;
+        const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) stage[r * 128 + wave * 32 + j * 16 + r16] = (uint8_t)e4m3_encode(h[mi][j][i] / sc);
+        if (wave == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + nt] = sc;
+      }
+    __syncthreads();
+    uint8_t* hq = reinterpret_cast<uint8_t*>(out);
+    for (int ci = tid; ci < BM * 8; ci += 256) {
+      const int r = ci >> 3, c = ci & 7;
+      if (m0 + r < m_end)
+        *reinterpret_cast<u32x4*>(hq + (long)(m0 + r) * ld_out + nt * 128 + c * 16) =
+            *reinterpret_cast<const u32x4*>(stage + r * 128 + c * 16);
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + mi * 16 + 4 * q + i;
+        if (m >= m_end) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = nt * 128 + wave * 32 + j * 16 + r16;
+          const float val = acc[mi][j][i];
+          if constexpr (EPI == kEpiF32) {
+            reinterpret_cast<float*>(out)[(long)m * ld_out + n] = val;
+          } else if constexpr (EPI == kEpiBf16) {
+            reinterpret_cast<uint16_t*>(out)[(long)m * ld_out + n] = f32_to_bf16_rne(val);
+          } else {
+            const long dst = dst_row ? (long)dst_row[m] : (long)m;
+            const float wgt = row_w ? row_w[m] : 1.0f;
+            atomicAdd(reinterpret_cast<float*>(out) + dst * ld_out + n, wgt * val);
+          }
+        }
+      }
+  }
+}
+
+template <int BM>
+static hipError_t launch_bm(const GemmArgs& args, int epi, hipStream_t st) {
+  const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
+  if (mt == 0) return hipSuccess;
+  int nt = 0;
+  const int nb = epi == kEpiSwiglu ? 2 : 1;
+  for (int s = 0; s < 2; ++s) {
+    const GemmSeg& S = args.seg[s];
+    if (S.m_tiles > 0) nt = nt > S.N / nb / 128 ? nt : S.N / nb / 128;
+  }
+  if (nt == 0) return hipSuccess;
+  const dim3 grid(mt, nt);
+  switch (epi) {
+    case kEpiSwiglu: grouped_gemm_kernel<BM, 2, kEpiSwiglu><<<grid, 256, 0, st>>>(args); break;
+    case kEpiF32: grouped_gemm_kernel<BM, 1, kEpiF32><<<grid, 256, 0, st>>>(args); break;
+    case kEpiBf16: grouped_gemm_kernel<BM, 1, kEpiBf16><<<grid, 256, 0, st>>>(args); break;
+    default: grouped_gemm_kernel<BM, 1, kEpiScatter><<<grid, 256, 0, st>>>(args); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st) {
+  switch (bm) {
+    case 16: return launch_bm<16>(args, epi, st);
+    case 32: return launch_bm<32>(args, epi, st);
+    case 64: return launch_bm<64>(args, epi, st);
+    default: return launch_bm<128>(args, epi, st);
+  }
+}
+
+int gemm_pick_bm(long rows_upper, int groups) {
+  const long avg = groups > 0 ? rows_upper / groups : rows_upper;
+  if (avg <= 16) return 16;
+  if (avg <= 32) return 32;
+  if (avg <= 64) return 64;
+  return 128;
+}
+
+}  // namespace moefp8

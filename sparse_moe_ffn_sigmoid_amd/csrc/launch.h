@@ -1,0 +1,63 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoefp8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moefp8 {
+
+enum Epi { kEpiF32 = 0, kEpiBf16 = 1, kEpiSwiglu = 2, kEpiScatter = 3 };
+
+// One segment of a grouped GEMM launch.  A static segment (offsets == nullptr)
+// is one group of m_rows rows; a dynamic one reads its G+1 row offsets on the
+// device.  Row m of group g multiplies B rows [0, N) of that group.
+struct GemmSeg {
+  const uint8_t* a_q;        // [*][K] e4m3
+  const float* a_s;          // [*][K/128]
+  const int32_t* a_gather;   // logical row -> source row, or nullptr
+  const uint8_t* b_q;        // [G][N][K]
+  const float* b_s;          // [G][N/128][K/128]
+  long long b_stride;        // N*K
+  long long bs_stride;       // (N/128)*(K/128)
+  const int32_t* offsets;    // [G+1] on the device, or nullptr (static)
+  int G;
+  int m_rows;                // static segment rows
+  int m_tiles;               // tiles reserved in the grid for this segment
+  int N;
+  int K;                     // % 128 == 0
+  void* out;                 // epilogue output
+  float* out_s;              // SwiGLU: scales [M][N/256]
+  int ld_out;                // elements per output row
+  const int32_t* dst_row;    // scatter: destination row per logical row (nullptr = identity)
+  const float* row_w;        // scatter: weight per logical row (nullptr = 1)
+};
+
+struct GemmArgs {
+  GemmSeg seg[2];            // seg[0] static (may be empty), seg[1] dynamic (may be empty)
+};
+
+hipError_t launch_quant_1x128(const void* x, bool bf16, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
+                              hipStream_t st);
+hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, hipStream_t st);
+hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,
+                        float routed_scale, int32_t* topk_idx, float* topk_w, hipStream_t st);
+size_t permute_scratch_bytes(int n, int E);
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* sorted_assign,
+                          int32_t* assign_pos, int32_t* sorted_token, const float* topk_w, float* sorted_w,
+                          int32_t* scratch, hipStream_t st);
+hipError_t launch_gather_rows(const void* rows_in, int row_bytes, int n, int k, const int32_t* sorted_assign,
+                              void* rows_out, hipStream_t st);
+hipError_t launch_combine(const float* y, const int32_t* ap, const float* w, const float* shared, int T, int k, int d,
+                          uint16_t* out, hipStream_t st);
+hipError_t launch_unpermute(const void* y, const int32_t* ap, long n, int row_bytes, void* out, hipStream_t st);
+hipError_t launch_cast_bf16(const float* in, long n, uint16_t* out, hipStream_t st);
+hipError_t launch_fill_zero(float* p, long n, hipStream_t st);
+
+// Grouped block-scaled GEMM.  bm = rows per tile (16, 32, 64 or 128); the
+// caller sets each segment's m_tiles for that bm.
+hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st);
+int gemm_pick_bm(long rows_upper, int groups);
+
+}  // namespace moefp8

@@ -1,0 +1,242 @@
+// Sorting token-expert assignments by expert (stable: by expert, then by
+// assignment index a = t*k + j) and the inverse / weighted combine.
+//
+// Deterministic three-pass counting sort over chunks of 1024 assignments:
+//   count   - per-chunk expert histogram (LDS atomics: counts do not depend on order);
+//   scan    - per expert, exclusive prefix over chunks; offsets = exclusive scan over experts;
+//   scatter - each wave ranks its 64 lanes among equal expert ids with ballots
+//             (lower lane first) and places them after everything earlier.
+#include "common.h"
+#include "launch.h"
+
+namespace moefp8 {
+
+constexpr int kChunk = 1024;          // assignments per workgroup (4 waves x 4 steps x 64 lanes)
+
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx, int n, int E,
+                                                         int32_t* __restrict__ chunk_counts) {
+  extern __shared__ int cnt[];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int a0 = c * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += 256) {
+    const int a = a0 + i;
+    if (a < n) atomicAdd(&cnt[idx[a]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(long)c * E + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads.  chunk_counts becomes the exclusive prefix over
+// chunks (per expert); offsets[e] = exclusive prefix over experts, offsets[E] = n.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunks, int E,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int tot[1024];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk_counts[(long)c * E + e];
+      chunk_counts[(long)c * E + e] = run;
+      run += v;
+    }
+  }
+  tot[e] = run;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive Hillis-Steele scan
+    const int v = e >= o ? tot[e - o] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) offsets[e] = tot[e] - run;
+  if (e == E - 1) offsets[E] = tot[e];
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ idx, int n, int k, int E,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_assign,
+                                                           int32_t* __restrict__ assign_pos,
+                                                           int32_t* __restrict__ sorted_token,
+                                                           const float* __restrict__ topk_w,
+                                                           float* __restrict__ sorted_w) {
+  extern __shared__ int wcnt[];      // [4][E]: per wave, then start position per (wave, expert)
+  const int c = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int* mycnt = wcnt + wave * E;
+  for (int e = lane; e < E; e += 64) mycnt[e] = 0;
+  __syncthreads();
+  const int a_wave = c * kChunk + wave * 256;
+  for (int s = 0; s < 4; ++s) {
+    const int a = a_wave + s * 64 + lane;
+    if (a < n) atomicAdd(&mycnt[idx[a]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = offsets[e] + chunk_base[(long)c * E + e];
+    for (int w = 0; w < 4; ++w) {
+      const int v = wcnt[w * E + e];
+      wcnt[w * E + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;   // enough bits for ids 0..E (E marks an idle lane)
+  for (int s = 0; s < 4; ++s) {
+    const int a = a_wave + s * 64 + lane;
+    const bool valid = a < n;
+    const int e = valid ? idx[a] : E;
+    unsigned long long peers = ~0ull;
+    for (int bit = 0; bit < nbits; ++bit) {
+      const unsigned long long m = __ballot((e >> bit) & 1);
+      peers &= ((e >> bit) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    const int gsize = __popcll(peers);
+    int pos = 0;
+    if (valid) pos = mycnt[e] + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == gsize - 1) mycnt[e] += gsize;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      sorted_assign[pos] = a;
+      assign_pos[a] = pos;
+      if (sorted_token) sorted_token[pos] = a / k;
+      if (sorted_w) sorted_w[pos] = topk_w[a];
+    }
+  }
+}
+
+// rows_out[p] = rows_in[sorted_assign[p] / k], row_bytes % 16 == 0.
+__global__ __launch_bounds__(256) void perm_gather_kernel(const uint4* __restrict__ rows_in, int row_vec, int n, int k,
+                                                          const int32_t* __restrict__ sorted_assign,
+                                                          uint4* __restrict__ rows_out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)n * row_vec;
+  if (i >= total) return;
+  const long p = i / row_vec;
+  const int c = (int)(i - p * row_vec);
+  rows_out[i] = rows_in[(long)(sorted_assign[p] / k) * row_vec + c];
+}
+
+// out[t][c] = bf16(sum_j w[t][j] * y[assign_pos[t*k+j]][c] (+ shared[t][c])), fp32, slot order.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ ap,
+                                                      const float* __restrict__ w, const float* __restrict__ shared,
+                                                      int T, int k, int d, uint16_t* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;       // one float4 of output per thread
+  const int dv = d >> 2;
+  if (i >= (long)T * dv) return;
+  const long t = i / dv;
+  const int c = (int)(i - t * dv) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const float4 v = *reinterpret_cast<const float4*>(y + (long)ap[t * k + j] * d + c);
+    acc.x = fmaf(wj, v.x, acc.x);
+    acc.y = fmaf(wj, v.y, acc.y);
+    acc.z = fmaf(wj, v.z, acc.z);
+    acc.w = fmaf(wj, v.w, acc.w);
+  }
+  if (shared) {
+    const float4 v = *reinterpret_cast<const float4*>(shared + t * d + c);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+  o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+  *reinterpret_cast<uint2*>(out + t * d + c) = o;
+}
+
+// out[t*k+j][:] = y[assign_pos[t*k+j]][:], rows of row_words 32-bit words.
+__global__ __launch_bounds__(256) void unpermute_kernel(const uint32_t* __restrict__ y, const int32_t* __restrict__ ap,
+                                                        long n, int row_words, uint32_t* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * row_words) return;
+  const long a = i / row_words;
+  const int c = (int)(i - a * row_words);
+  out[i] = y[(long)ap[a] * row_words + c];
+}
+
+// acc (fp32) -> bf16, round to nearest even.
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ in, long n4, uint16_t* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = reinterpret_cast<const float4*>(in)[i];
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+  o.y = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+  reinterpret_cast<uint2*>(out)[i] = o;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, long n4) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+size_t permute_scratch_bytes(int n, int E) {
+  const long nchunks = (n + kChunk - 1) / kChunk;
+  return (size_t)nchunks * E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* sorted_assign,
+                          int32_t* assign_pos, int32_t* sorted_token, const float* topk_w, float* sorted_w,
+                          int32_t* scratch, hipStream_t st) {
+  const int n = T * k;
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  if (nchunks > 0) perm_count_kernel<<<nchunks, 256, E * sizeof(int), st>>>(idx, n, E, scratch);
+  perm_scan_kernel<<<1, 1024, 0, st>>>(scratch, nchunks, E, offsets);
+  if (nchunks > 0)
+    perm_scatter_kernel<<<nchunks, 256, 4 * E * sizeof(int), st>>>(idx, n, k, E, scratch, offsets, sorted_assign,
+                                                                    assign_pos, sorted_token, topk_w, sorted_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* rows_in, int row_bytes, int n, int k, const int32_t* sorted_assign,
+                              void* rows_out, hipStream_t st) {
+  const int row_vec = row_bytes / 16;
+  const long total = (long)n * row_vec;
+  if (total == 0) return hipSuccess;
+  perm_gather_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
+      reinterpret_cast<const uint4*>(rows_in), row_vec, n, k, sorted_assign, reinterpret_cast<uint4*>(rows_out));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y, const int32_t* ap, const float* w, const float* shared, int T, int k, int d,
+                          uint16_t* out, hipStream_t st) {
+  const long total = (long)T * (d / 4);
+  if (total == 0) return hipSuccess;
+  combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(y, ap, w, shared, T, k, d, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const void* y, const int32_t* ap, long n, int row_bytes, void* out, hipStream_t st) {
+  const int row_words = row_bytes / 4;
+  const long total = n * row_words;
+  if (total == 0) return hipSuccess;
+  unpermute_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint32_t*>(y), ap, n,
+                                                                     row_words, reinterpret_cast<uint32_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* in, long n, uint16_t* out, hipStream_t st) {
+  const long n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  cast_bf16_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(in, n4, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, long n, hipStream_t st) {
+  const long n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  fill_zero_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+}  // namespace moefp8

@@ -1,0 +1,120 @@
+// Fine-granularity FP8 quantisation kernels (onlylabs "DeepSeek v3 and R1 Model
+// Architecture", headings "Fine granularity quantization" and "Online
+// Quantization"; aguasto "DeepSeek-R1", "Quantization": blockwise FP8).
+//
+// Per tile: amax = max |v|, s = fp32(amax / 448) (correctly rounded division),
+// q = e4m3(fp32(v / s)); an all-zero tile has s = 1.
+#include "common.h"
+#include "launch.h"
+
+namespace moefp8 {
+
+// One 16-lane group per 128-wide tile, 8 consecutive elements per lane
+// (one 16-byte load for bf16, two for fp32; one 8-byte store of codes).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int rows, int cols, int ld_x,
+                                                          uint8_t* __restrict__ q, int ld_q, float* __restrict__ s) {
+  const int tpr = cols >> 7;
+  const long ntiles = (long)rows * tpr;
+  const long tile = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool valid = tile < ntiles;
+  const long r = valid ? tile / tpr : 0;
+  const int tc = valid ? (int)(tile - r * tpr) : 0;
+  const int c0 = tc * 128 + sub * 8;
+  float v[8];
+  if (valid) {
+    if (kBf16) {
+      const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + r * ld_x + c0);
+      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + r * ld_x + c0);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = group_max<16>(amax);
+  const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / sc) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / sc) << (8 * i);
+  if (valid) {
+    *reinterpret_cast<uint2*>(q + r * ld_q + c0) = make_uint2(lo, hi);
+    if (sub == 0) s[r * tpr + tc] = sc;
+  }
+}
+
+// One workgroup per 128x128 block; thread t holds row t/2, columns (t%2)*64 .. +64;
+// the block's amax is reduced per wave, then across the 4 waves through LDS.
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restrict__ w, int rows, int cols,
+                                                            uint8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ float red[4];
+  const int bc = blockIdx.x, br = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int rr = tid >> 1;
+  const int cc = (tid & 1) * 64;
+  const float* src = w + (long)(br * 128 + rr) * cols + bc * 128 + cc;
+  float v[64];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 a = reinterpret_cast<const float4*>(src)[i];
+    v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+  uint8_t* dst = q + (long)(br * 128 + rr) * cols + bc * 128 + cc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t wd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) word |= e4m3_encode(v[16 * i + 4 * j + b] / sc) << (8 * b);
+      wd[j] = word;
+    }
+    reinterpret_cast<uint4*>(dst)[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+  if (tid == 0) s[br * (cols >> 7) + bc] = sc;
+}
+
+hipError_t launch_quant_1x128(const void* x, bool bf16, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
+                              hipStream_t st) {
+  const long ntiles = (long)rows * (cols / 128);
+  if (ntiles == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((ntiles + 15) / 16);
+  if (bf16)
+    quant_1x128_kernel<true><<<grid, 256, 0, st>>>(x, rows, cols, ld_x, q, ld_q, s);
+  else
+    quant_1x128_kernel<false><<<grid, 256, 0, st>>>(x, rows, cols, ld_x, q, ld_q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid(cols / 128, rows / 128);
+  quant_128x128_kernel<<<grid, 256, 0, st>>>(w, rows, cols, q, s);
+  return hipGetLastError();
+}
+
+}  // namespace moefp8

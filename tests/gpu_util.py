@@ -1,0 +1,126 @@
+"""Shared helpers of the GPU parity tests: building layers on the device and
+on the oracle side from the same fp32 weights, and the comparison bars."""
+from __future__ import annotations
+
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import synth
+from oracle import ffn, route
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def bf16_np(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor -> fp32 numpy values."""
+    return t.float().cpu().numpy()
+
+
+def output_bar(got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
+    """(relative L2, max |diff| / RMS) of the bf16 output against the bf16-rounded oracle."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.abs(got - ref).max() / max(np.sqrt(np.mean(ref ** 2)), 1e-300)) if ref.size else 0.0
+    return rel, mx
+
+
+def assert_output(got, ref, what=""):
+    rel, mx = output_bar(got, ref)
+    say(f"  {what}: rel L2 {rel:.3e}, max/RMS {mx:.3e}")
+    assert rel <= 1e-3, f"{what}: relative L2 {rel:.3e} > 1e-3"
+    assert mx <= 2e-2, f"{what}: max/RMS {mx:.3e} > 2e-2"
+
+
+class Layer:
+    """One layer's weights on both sides.  Small shapes draw numpy weights
+    (synth.gen_expert_w); V3 shapes draw them on the device with torch.  The
+    GPU side quantises with fp8_quant_128x128, the oracle with its own
+    quant_128x128, from the same fp32 values."""
+
+    def __init__(self, shape: synth.MoeShape, device_draw: bool | None = None, bias: np.ndarray | None = None):
+        import sparse_moe_ffn_sigmoid_amd as moe
+        self.s = shape
+        self.device_draw = shape.hidden >= 4096 if device_draw is None else device_draw
+        self.cfg = moe.MoeConfig.of(shape)
+        E = shape.n_experts
+        self._np_cache: dict[int, tuple[np.ndarray, np.ndarray]] = {}
+        self._oracle: dict[int, ffn.QuantExpert] = {}
+        w13q, w13s, w2q, w2s = [], [], [], []
+        for e in range(E + (1 if shape.n_shared else 0)):
+            w13, w2 = self._fp32_dev(e)
+            a, b = moe.fp8_quant_128x128(w13)
+            c, d = moe.fp8_quant_128x128(w2)
+            del w13, w2
+            w13q.append(a); w13s.append(b); w2q.append(c); w2s.append(d)
+        kw = {}
+        if E:
+            kw = dict(w13_q=torch.stack(w13q[:E]), w13_s=torch.stack(w13s[:E]), w2_q=torch.stack(w2q[:E]),
+                      w2_s=torch.stack(w2s[:E]))
+            del w13q[:E], w13s[:E], w2q[:E], w2s[:E]
+        if shape.n_shared:
+            kw.update(sh_w13_q=w13q[-1], sh_w13_s=w13s[-1], sh_w2_q=w2q[-1], sh_w2_s=w2s[-1])
+        self.wr_bits = synth.gen_router_w(shape) if E else None
+        self.bias = bias
+        if E:
+            kw["w_router"] = to_dev(self.wr_bits)
+            if bias is not None:
+                kw["bias"] = to_dev(bias.astype(np.float32))
+        self.weights = moe.MoeWeights(**kw)
+        torch.cuda.synchronize()
+
+    def _fp32_host(self, e: int) -> tuple[np.ndarray, np.ndarray]:
+        if self.device_draw:
+            w13 = synth.torch_expert_weight(self.s, e, "w13", DEV).cpu().numpy()
+            w2 = synth.torch_expert_weight(self.s, e, "w2", DEV).cpu().numpy()
+            return w13, w2
+        return synth.gen_expert_w(self.s, e)
+
+    def _fp32_dev(self, e: int):
+        if self.device_draw:
+            return synth.torch_expert_weight(self.s, e, "w13", DEV), synth.torch_expert_weight(self.s, e, "w2", DEV)
+        w13, w2 = synth.gen_expert_w(self.s, e)
+        return to_dev(w13), to_dev(w2)
+
+    def oracle_experts(self, ids) -> None:
+        """Quantise the given experts on the oracle side (threads: numpy releases the GIL)."""
+        todo = sorted(set(int(i) for i in ids) - set(self._oracle))
+        host = {e: self._fp32_host(e) for e in todo}           # device draws happen on this thread
+        with ThreadPoolExecutor(16) as ex:
+            res = ex.map(lambda e: (e, ffn.quantize_expert(*host[e])), todo)
+            for e, q in res:
+                self._oracle[e] = q
+                del host[e]
+
+    def expert(self, e: int) -> ffn.QuantExpert:
+        if e not in self._oracle:
+            self.oracle_experts([e])
+        return self._oracle[e]
+
+    def oracle_forward(self, x_vals: np.ndarray, scores: np.ndarray | None = None) -> dict:
+        s = self.s
+        if s.n_experts:
+            if scores is None:
+                scores = route.sigmoid_scores(route.router_logits(x_vals, synth.bf16_bits_to_f32(self.wr_bits)))
+            idx, _ = route.select(scores, self.bias, s.n_group, s.topk_group, s.top_k, s.routed_scale)
+            self.oracle_experts(list(np.unique(idx)) + [s.n_experts] if s.n_shared else list(np.unique(idx)))
+        else:
+            self.oracle_experts([0])
+        return ffn.moe_ffn(x_vals, s.n_experts, s.top_k, s.n_group, s.topk_group, self.expert, scores=scores,
+                           bias=self.bias, n_shared=s.n_shared, routed_scale=s.routed_scale,
+                           w_router=None if scores is not None else synth.bf16_bits_to_f32(self.wr_bits))

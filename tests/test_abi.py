@@ -1,0 +1,147 @@
+"""Host-side checks of libmoefp8.so (no GPU needed): the library loads, exports
+every entry point the header declares, sizes workspaces, and rejects bad
+arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_ffn_sigmoid_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moefp8.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_moe_ffn_sigmoid_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^MOE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert names == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(-3) == b"MOE_ERR_WORKSPACE"
+    assert lib.moe_status_string(7) == b"MOE_ERR_UNKNOWN"
+
+
+def _cfg(**kw):
+    base = dict(hidden=7168, inter=2048, n_experts=256, top_k=8, n_shared=1, inter_shared=2048, n_group=8,
+                topk_group=4, group_score=0, routed_scale=1.0)
+    base.update(kw)
+    return _lib.MoeCfgC(**base)
+
+
+def test_workspace_sizes(lib):
+    c = _cfg()
+    n64 = lib.moe_ffn_workspace_size(64, ctypes.byref(c))
+    n4k = lib.moe_ffn_workspace_size(4096, ctypes.byref(c))
+    assert n64 > 0 and n4k > 60 * n64 // 2
+    # fp32 sorted-row outputs dominate: T*k*d*4 bytes
+    assert n4k >= 4096 * 8 * 7168 * 4
+    assert lib.moe_ffn_workspace_size(-1, ctypes.byref(c)) == 0
+    bad = _cfg(n_group=7)
+    assert lib.moe_ffn_workspace_size(64, ctypes.byref(bad)) == 0
+    dense = _cfg(n_experts=0, top_k=0, inter=0, inter_shared=18432)
+    assert lib.moe_ffn_workspace_size(4096, ctypes.byref(dense)) >= 4096 * 18432
+    assert lib.moe_permute_workspace_size(4096, 8, 256) == 32 * 256 * 4
+    assert lib.moe_permute_workspace_size(10, 8, 2000) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned non-null: never dereferenced (checks fail first)
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_quant_argument_checks(lib):
+    assert lib.fp8_quant_1x128(FAKE, 1, 4, 100, 100, FAKE, 100, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert "multiple of 128" in _err(lib)
+    assert lib.fp8_quant_1x128(FAKE, 5, 4, 128, 128, FAKE, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.fp8_quant_1x128(None, 1, 4, 128, 128, FAKE, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.fp8_quant_1x128(FAKE, 1, 4, 128, 64, FAKE, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.fp8_quant_1x128(ctypes.c_void_p(0x10008), 1, 4, 128, 128, FAKE, 128, FAKE, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert lib.fp8_quant_1x128(None, 1, 0, 128, 128, None, 128, None, None) == _lib.MOE_OK   # empty: no-op
+    assert lib.fp8_quant_128x128(FAKE, 130, 128, FAKE, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_group=7), _lib.MOE_ERR_UNSUPPORTED_SHAPE),          # 256 % 7 != 0
+    (dict(topk_group=9), _lib.MOE_ERR_INVALID_ARG),             # > n_group
+    (dict(top_k=200), _lib.MOE_ERR_INVALID_ARG),                # > topk_group * E / n_group
+    (dict(topk_group=1, top_k=33), _lib.MOE_ERR_INVALID_ARG),   # > 1 * 32
+    (dict(n_experts=2048, n_group=8), _lib.MOE_ERR_UNSUPPORTED_SHAPE),
+    (dict(group_score=3), _lib.MOE_ERR_INVALID_ARG),
+])
+def test_route_config_checks(lib, kw, code):
+    c = _cfg(**kw)
+    assert lib.moe_route(FAKE, FAKE, None, 4, ctypes.byref(c), FAKE, 0, FAKE, FAKE, None) == code
+
+
+def test_route_needs_router_weights_without_given_scores(lib):
+    c = _cfg()
+    assert lib.moe_route(None, None, None, 4, ctypes.byref(c), FAKE, 0, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, None, None, 0, ctypes.byref(c), None, 0, None, None, None) == _lib.MOE_OK
+    assert lib.moe_route(FAKE, FAKE, None, 4, ctypes.byref(c), FAKE, 8, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_permute_checks(lib):
+    assert lib.moe_permute(FAKE, 4, 2, 2000, FAKE, FAKE, FAKE, None, 0, None, FAKE, 1 << 20, None) == \
+        _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert lib.moe_permute(FAKE, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 1 << 20, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(FAKE, 4, 2, 16, FAKE, FAKE, FAKE, FAKE, 24, FAKE, FAKE, 1 << 20, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(FAKE, 4096, 8, 256, FAKE, FAKE, FAKE, None, 0, None, FAKE, 100, None) == \
+        _lib.MOE_ERR_WORKSPACE
+
+
+def test_gemm_checks(lib):
+    epi = _lib.MoeEpiC(None, None, None)
+    args = [FAKE, FAKE, None, FAKE, FAKE, FAKE]
+    assert lib.fp8_grouped_gemm_blockscaled(*args, 4, 64, 200, 128, 0, ctypes.byref(epi), FAKE, None) == \
+        _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert lib.fp8_grouped_gemm_blockscaled(*args, 4, 64, 384, 128, 2, ctypes.byref(epi), FAKE, None) == \
+        _lib.MOE_ERR_INVALID_ARG                                    # SwiGLU needs N % 256 and h_s
+    assert lib.fp8_grouped_gemm_blockscaled(*args, 0, 64, 256, 128, 0, ctypes.byref(epi), FAKE, None) == \
+        _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert lib.fp8_grouped_gemm_blockscaled(*args, 4, 64, 256, 128, 9, ctypes.byref(epi), FAKE, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+
+
+def test_forward_checks(lib):
+    c = _cfg()
+    w = _lib.MoeWeightsC(*([0x10000] * 10))
+    need = lib.moe_ffn_workspace_size(64, ctypes.byref(c))
+    assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(c), ctypes.byref(w), FAKE, need - 1, FAKE, None, None, None, 0,
+                               None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(c), ctypes.byref(w), ctypes.c_void_p(0x10010), need, FAKE, None,
+                               None, None, 0, None) == _lib.MOE_ERR_WORKSPACE                   # not 256-aligned
+    assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(c), ctypes.byref(w), FAKE, need, FAKE, None, None, None, 0x10,
+                               None) == _lib.MOE_ERR_INVALID_ARG                                # unknown flag
+    w0 = _lib.MoeWeightsC(*([0x10000] * 2 + [0] * 8))
+    assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(c), ctypes.byref(w0), FAKE, need, FAKE, None, None, None, 0,
+                               None) == _lib.MOE_ERR_INVALID_ARG                                # no expert weights
+    assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(c), ctypes.byref(w), FAKE, need, FAKE, None, None, None, 1,
+                               None) == _lib.MOE_ERR_INVALID_ARG                                # scores given but NULL
+    dense_bad = _cfg(n_experts=0, n_shared=0)
+    assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(dense_bad), ctypes.byref(w), FAKE, need, FAKE, None, None, None,
+                               0, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_ffn_forward(None, 0, ctypes.byref(c), ctypes.byref(w), None, 0, None, None, None, None, 0, None) == \
+        _lib.MOE_OK

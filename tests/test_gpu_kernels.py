@@ -1,0 +1,250 @@
+"""GPU parity of each C-ABI call against the oracle (bit-exact where the method
+fixes the result: FP8 codes and scales, expert sets and weights given the
+scores, permutation and offsets)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import e4m3, gemm, permute, quant, route
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import sparse_moe_ffn_sigmoid_amd as moe
+    from gpu_util import DEV, say, to_dev
+
+
+def _adversarial_rows(seed, rows, cols):
+    r = np.random.default_rng(seed)
+    v = r.standard_normal((rows, cols)).astype(np.float32)
+    v[0] = 0.0                                                   # all-zero row
+    v[1] *= np.float32(1e-30)                                    # tiny values (subnormal quotients)
+    v[2] *= np.float32(1e30)
+    v[3] = np.exp2(r.uniform(-40, 40, cols)).astype(np.float32)  # huge dynamic range inside tiles
+    v[4, ::2] = np.float32(-0.0)
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 384), (512, 7168)])
+def test_quant_1x128_bit_exact(dtype, rows, cols):
+    say(f"quant_1x128 {dtype} {rows}x{cols}")
+    v = _adversarial_rows(rows * 7 + cols, rows, cols) if rows > 4 else \
+        np.random.default_rng(1).standard_normal((rows, cols)).astype(np.float32)
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(v)
+        v = synth.bf16_bits_to_f32(bits)
+        xd = to_dev(bits)
+    else:
+        xd = to_dev(v)
+    q, s = moe.fp8_quant_1x128(xd)
+    want_q, want_s = quant.quant_1x128(v)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), want_q)
+
+
+def test_e4m3_encoder_every_midpoint_and_random_fp32():
+    """Tiles whose amax is exactly 448 have s = 1, so every other element is
+    encoded as is: probe grid values, midpoints, their fp32 neighbours and
+    random fp32 bit patterns of magnitude <= 448."""
+    vals, _ = e4m3.finite_positive_grid()
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    probe = np.concatenate([vals.astype(np.float32), mids, np.nextafter(mids, np.float32(0)),
+                            np.nextafter(mids, np.float32(1000))])
+    r = np.random.default_rng(5)
+    bits = r.integers(0, 0x43E00000, size=400000, dtype=np.uint32)        # every fp32 pattern below 448
+    probe = np.concatenate([probe, bits.view(np.float32)])
+    probe = np.concatenate([probe, -probe])
+    n = -(-probe.size // 127) * 127
+    probe = np.concatenate([probe, np.zeros(n - probe.size, np.float32)])
+    tiles = np.concatenate([np.full((n // 127, 1), 448.0, np.float32), probe.reshape(-1, 127)], axis=1)
+    q, s = moe.fp8_quant_1x128(to_dev(np.ascontiguousarray(tiles)))
+    assert np.all(s.cpu().numpy() == 1.0)
+    assert np.array_equal(q.cpu().numpy(), e4m3.encode(tiles))
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (4096, 7168)])
+def test_quant_128x128_bit_exact(rows, cols):
+    say(f"quant_128x128 {rows}x{cols}")
+    r = np.random.default_rng(rows + cols)
+    w = (r.standard_normal((rows, cols)) * np.exp2(r.integers(-10, 10, (rows, 1)))).astype(np.float32)
+    w[:128, :128] = 0.0
+    q, s = moe.fp8_quant_128x128(to_dev(w))
+    want_q, want_s = quant.quant_128x128(w)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), want_q)
+
+
+ROUTE_CASES = [
+    # (T, E, k, G, gk, ties, bias scale, rule)
+    (64, 16, 2, 4, 2, False, 0.0, 0),
+    (300, 16, 2, 4, 2, True, 0.0, 0),
+    (4096, 256, 8, 8, 4, False, 0.0, 0),
+    (4096, 256, 8, 8, 4, False, 0.3, 0),
+    (1000, 256, 8, 8, 4, True, 0.0, 0),
+    (777, 64, 6, 8, 8, False, 0.2, 0),
+    (500, 96, 4, 3, 2, True, 0.1, 1),
+    (129, 1024, 16, 32, 4, False, 0.05, 0),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES)
+def test_route_given_scores_bit_exact(case):
+    T, E, k, G, gk, ties, bscale, rule = case
+    say(f"moe_route scores given T={T} E={E} k={k} G={G} gk={gk} ties={ties} bias={bscale} rule={rule}")
+    sc = synth.gen_scores(T, E, cfg_id=E + k, ties=ties)
+    bias = synth.gen_bias(E, scale=bscale) if bscale else None
+    cfg = moe.MoeConfig(128, 128, E, k, 0, 0, G, gk, rule, 1.0)
+    _, idx, w = moe.moe_route(cfg, T, DEV, scores=to_dev(sc), bias=None if bias is None else to_dev(bias))
+    want_idx, want_w = route.select(sc, bias, G, gk, k, 1.0, "max" if rule else "top2_sum")
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), want_w.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [synth.TINY, synth.with_tokens(synth.V3_PREFILL, 1000)])
+def test_router_scores(shape):
+    say(f"router scores {shape.name} T={shape.tokens}")
+    xb = synth.gen_x(shape)
+    wr = synth.gen_router_w(shape)
+    cfg = moe.MoeConfig.of(shape)
+    sc, idx, _ = moe.moe_route(cfg, shape.tokens, DEV, x=to_dev(xb), w_router=to_dev(wr))
+    want = route.sigmoid_scores(route.router_logits(synth.bf16_bits_to_f32(xb), synth.bf16_bits_to_f32(wr)))
+    got = sc.cpu().numpy()
+    # fp32 accumulation of d products of bf16 values (|logit| ~ 1.7): a few 1e-6
+    assert np.abs(got - want).max() <= 2e-5
+    # expert sets: equal except where the oracle's own scores are within rounding of a tie
+    want_idx, _ = route.select(want, None, shape.n_group, shape.topk_group, shape.top_k)
+    gi = np.sort(idx.cpu().numpy(), 1)
+    wi = np.sort(want_idx, 1)
+    diff = np.flatnonzero((gi != wi).any(1))
+    assert diff.size <= max(1, shape.tokens // 100)
+    for t in diff:
+        assert abs(float(want[t, gi[t]].astype(np.float64).sum() - want[t, wi[t]].astype(np.float64).sum())) < 1e-4
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (64, 2, 16), (64, 8, 256), (1000, 4, 7), (4096, 8, 256),
+                                   (16384, 8, 256), (333, 3, 1024)])
+def test_permute_bit_exact(T, k, E):
+    say(f"moe_permute T={T} k={k} E={E}")
+    r = np.random.default_rng(T + E)
+    keys = r.random((T, E))
+    keys[: T // 3, 0] = -1.0                                     # load skew: expert 0 first for a third of the tokens
+    idx = np.argsort(keys, axis=1)[:, :k].astype(np.int32)
+    rows = r.integers(0, 256, (T, 48), dtype=np.uint8)
+    off, sa, ap, g = moe.moe_permute(to_dev(idx), E, rows=to_dev(rows))
+    w_off, w_sa, w_ap = permute.permute(idx, E)
+    assert np.array_equal(off.cpu().numpy(), w_off)
+    assert np.array_equal(sa.cpu().numpy(), w_sa)
+    assert np.array_equal(ap.cpu().numpy(), w_ap)
+    assert np.array_equal(g.cpu().numpy(), permute.gather_rows(rows, w_sa, k))
+    back = moe.moe_unpermute(g, ap, k)
+    assert np.array_equal(back.cpu().numpy(), np.repeat(rows[:, None, :], k, axis=1))
+
+
+def test_permute_empty_and_all_to_one():
+    say("moe_permute T=0 and all tokens on one expert")
+    off, sa, ap, _ = moe.moe_permute(torch.zeros((0, 4), dtype=torch.int32, device=DEV), 8)
+    assert off.cpu().numpy().tolist() == [0] * 9
+    idx = np.full((3000, 1), 5, np.int32)
+    off, sa, ap, _ = moe.moe_permute(to_dev(idx), 8)
+    assert off.cpu().numpy().tolist() == [0, 0, 0, 0, 0, 0, 3000, 3000, 3000]
+    assert np.array_equal(sa.cpu().numpy(), np.arange(3000))
+
+
+def test_unpermute_weighted_combine():
+    say("moe_unpermute weighted combine")
+    r = np.random.default_rng(9)
+    T, k, E, d = 300, 4, 32, 512
+    idx = np.argsort(r.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    _, _, ap = permute.permute(idx, E)
+    y = r.standard_normal((T * k, d)).astype(np.float32)
+    w = r.random((T, k)).astype(np.float32)
+    sh = r.standard_normal((T, d)).astype(np.float32)
+    out = moe.moe_unpermute(to_dev(y), to_dev(ap), k, topk_w=to_dev(w), shared_y=to_dev(sh))
+    ref = np.asarray(permute.combine(y, ap, w, sh))
+    from oracle.ffn import round_bf16
+    got = out.float().cpu().numpy()
+    assert np.abs(got - round_bf16(ref)).max() <= np.abs(ref).max() * 2.0 ** -7
+
+
+def _gemm_case(seed, M_groups, N, K, gather_rows=None):
+    r = np.random.default_rng(seed)
+    G = len(M_groups)
+    M = int(sum(M_groups))
+    src = gather_rows or M
+    a = r.standard_normal((src, K)).astype(np.float32)
+    a_q, a_s = quant.quant_1x128(a)
+    bws = [(r.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32) for _ in range(G)]
+    bq = [quant.quant_128x128(b) for b in bws]
+    b_q = np.stack([x[0] for x in bq])
+    b_s = np.stack([x[1] for x in bq])
+    offsets = np.concatenate([[0], np.cumsum(M_groups)]).astype(np.int32)
+    gather = r.integers(0, src, M).astype(np.int32) if gather_rows else None
+    return a_q, a_s, b_q, b_s, offsets, gather
+
+
+GEMM_CASES = [
+    ([16], 128, 128, None),
+    ([1, 0, 37, 5, 130, 0, 64], 256, 384, None),
+    ([300, 2, 0, 77], 512, 256, 120),
+    ([2000], 384, 512, None),
+    ([3] * 40, 256, 256, 50),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES)
+def test_grouped_gemm_store_f32(case):
+    mg, N, K, gr = case
+    say(f"grouped GEMM f32 groups={mg[:8]} N={N} K={K} gather={gr}")
+    a_q, a_s, b_q, b_s, off, gat = _gemm_case(len(mg) + N, mg, N, K, gr)
+    out = moe.fp8_grouped_gemm_blockscaled(to_dev(a_q), to_dev(a_s), to_dev(b_q), to_dev(b_s), to_dev(off),
+                                           moe.MOE_EPI_STORE_F32, a_gather=None if gat is None else to_dev(gat),
+                                           m_max=int(off[-1]))
+    ref = gemm.grouped_gemm_blockscaled(a_q, a_s, gat, b_q, b_s, off)
+    got = out.cpu().numpy().astype(np.float64)
+    scale = np.abs(ref).max() + 1e-30
+    assert np.abs(got - ref).max() <= 2e-5 * scale, np.abs(got - ref).max() / scale
+
+
+def test_grouped_gemm_bf16_and_scatter():
+    say("grouped GEMM bf16 + weighted scatter-add")
+    mg = [5, 0, 70, 33]
+    N, K = 256, 256
+    a_q, a_s, b_q, b_s, off, _ = _gemm_case(77, mg, N, K)
+    args = [to_dev(a_q), to_dev(a_s), to_dev(b_q), to_dev(b_s), to_dev(off)]
+    ref = gemm.grouped_gemm_blockscaled(a_q, a_s, None, b_q, b_s, off)
+    out = moe.fp8_grouped_gemm_blockscaled(*args, moe.MOE_EPI_STORE_BF16, m_max=int(off[-1]))
+    from oracle.ffn import round_bf16
+    got = out.float().cpu().numpy()
+    assert np.abs(got - round_bf16(ref)).max() <= np.abs(ref).max() * 2.0 ** -8
+    r = np.random.default_rng(3)
+    M = int(off[-1])
+    dst = r.integers(0, 20, M).astype(np.int32)
+    wt = r.random(M).astype(np.float32)
+    acc = moe.fp8_grouped_gemm_blockscaled(*args, moe.MOE_EPI_WEIGHTED_SCATTER_ADD, m_max=M, dst_row=to_dev(dst),
+                                           row_weight=to_dev(wt), out_rows=20)
+    want = np.zeros((20, N))
+    np.add.at(want, dst, wt[:, None].astype(np.float64) * ref)
+    assert np.abs(acc.cpu().numpy() - want).max() <= 2e-5 * np.abs(want).max()
+
+
+@pytest.mark.parametrize("mg,W,K", [([7, 0, 130], 128, 256), ([64] * 5, 256, 512), ([1000], 128, 384)])
+def test_grouped_gemm_swiglu_quant(mg, W, K):
+    say(f"grouped GEMM SwiGLU+quant groups={mg} W={W} K={K}")
+    a_q, a_s, b_q, b_s, off, _ = _gemm_case(W + K, mg, 2 * W, K)
+    h_q, h_s = moe.fp8_grouped_gemm_blockscaled(to_dev(a_q), to_dev(a_s), to_dev(b_q), to_dev(b_s), to_dev(off),
+                                                moe.MOE_EPI_SWIGLU_QUANT, m_max=int(off[-1]))
+    gu = gemm.grouped_gemm_blockscaled(a_q, a_s, None, b_q, b_s, off)
+    from oracle.ffn import silu
+    h = (silu(gu[:, :W]) * gu[:, W:]).astype(np.float32)
+    want_q, want_s = quant.quant_1x128(h)
+    got_q, got_s = h_q.cpu().numpy(), h_s.cpu().numpy()
+    # fp32 accumulation differs from fp64 by ~1e-6 relative: scales within a few ulps,
+    # codes equal except at rounding midpoints (then one step apart)
+    assert np.allclose(got_s, want_s, rtol=1e-5, atol=0)
+    mism = got_q != want_q
+    assert mism.mean() <= 2e-3, mism.mean()
+    deq_got = quant.dequant_1x128(got_q, got_s)
+    srep = np.repeat(got_s.astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(deq_got - h) <= e4m3.half_ulp(np.abs(h) / srep) * srep * 1.01 + 1e-6 * np.abs(h) + 1e-30)
