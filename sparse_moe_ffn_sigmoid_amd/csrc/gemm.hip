@@ -8,6 +8,16 @@
 // e4m3 -> fp32) per 16x16 output tile.  Each block's partial is promoted into
 // the fp32 accumulator with one FMA per element: acc = fma(part, sa * sb, acc).
 //
+// Accumulation precision: measured on MI355X, the FP8 MFMAs (this one and the
+// 16x16x32 form alike) return a 128-term dot product with a relative error
+// near 1e-5 of the sum of |products|, while the bf16 MFMA sums exactly decoded
+// e4m3 values as an IEEE fp32 accumulation would.  Where the GEMM's output is
+// requantised to e4m3 (the gate/up GEMM with the SwiGLU epilogue), 1e-5 shifts
+// flip codes at rounding midpoints often enough to cost ~1e-3 of the layer's
+// output, so that GEMM converts both tiles to bf16 in registers (exact) and runs
+// four 16x16x32 bf16 MFMAs per K block instead ("exact" path).  The down GEMM,
+// whose output is not requantised, keeps the native FP8 MFMA.
+//
 // Workgroup: 4 waves, BM rows x (128 * NB) B rows.  Every wave covers all BM
 // rows and 32 of each 128-row B block, so with NB = 2 (the gate/up GEMM, B rows
 // [gate block; up block]) a lane holds gate and up values of the same (row,
@@ -46,6 +56,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
   constexpr int A_CH = BM * 8;                // 16-byte chunks per K block
   constexpr int A_PER = (A_CH + 255) / 256;
   constexpr int B_PER = BN * 8 / 256;
+  constexpr bool kExact = EPI == kEpiSwiglu;   // requantised output: exact-accumulating bf16 MFMA
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::kStage];
   __shared__ int scan_tmp[256];
   __shared__ int pre[1024];
@@ -207,12 +218,34 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
     const float* sa = reinterpret_cast<const float*>(st + TL::kA + TL::kB);
     const float* sb = reinterpret_cast<const float*>(st + TL::kA + TL::kB + TL::kSA);
     v4f part[MT][NT];
+    if constexpr (kExact) {
+      // lane bytes [8j, 8j+8) of its 32 feed bf16 MFMA j: the same K mapping on both operands
+      v8bf ab[MT][4], bb[NT][4];
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ab[mi][j] = e4m3x8_to_bf16((uint32_t)af[mi][2 * j], (uint32_t)af[mi][2 * j + 1]);
 #pragma unroll
       for (int nj = 0; nj < NT; ++nj)
-        part[mi][nj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[nj], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bb[nj][j] = e4m3x8_to_bf16((uint32_t)bf[nj][2 * j], (uint32_t)bf[nj][2 * j + 1]);
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NT; ++nj) {
+          v4f p = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[mi][j], bb[nj][j], p, 0, 0, 0);
+          part[mi][nj] = p;
+        }
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NT; ++nj)
+          part[mi][nj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[nj], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                           0, 0, 0, 0, 0, 0);
+    }
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       const float4 s4 = *reinterpret_cast<const float4*>(sa + mi * 16 + 4 * q);

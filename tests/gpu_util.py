@@ -31,18 +31,30 @@ def bf16_np(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy()
 
 
-def output_bar(got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
-    """(relative L2, max |diff| / RMS) of the bf16 output against the bf16-rounded oracle."""
+def output_bar(got: np.ndarray, ref_bf16: np.ndarray, ref_f64: np.ndarray) -> tuple[float, float, float]:
+    """The output bar of the layer:
+    relative L2 of the bf16 output against the oracle's bf16-rounded output (bf16
+    rounding alone costs ~1.7e-3 in L2 against the unrounded value), and max
+    |diff| / RMS per element against the oracle's unrounded fp64 output (against
+    the rounded one, a single 1-ulp rounding disagreement on an element above
+    4 x RMS already exceeds 2e-2 x RMS).  Also returns max/RMS against the
+    rounded output, for the record."""
     got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
-    mx = float(np.abs(got - ref).max() / max(np.sqrt(np.mean(ref ** 2)), 1e-300)) if ref.size else 0.0
-    return rel, mx
+    rb = np.asarray(ref_bf16, np.float64)
+    rf = np.asarray(ref_f64, np.float64)
+    rms = max(float(np.sqrt(np.mean(rf ** 2))), 1e-300) if rf.size else 1.0
+    rel = float(np.linalg.norm(got - rb) / max(np.linalg.norm(rb), 1e-300))
+    mx = float(np.abs(got - rf).max() / rms) if rf.size else 0.0
+    mx_rounded = float(np.abs(got - rb).max() / rms) if rf.size else 0.0
+    return rel, mx, mx_rounded
 
 
-def assert_output(got, ref, what=""):
-    rel, mx = output_bar(got, ref)
-    say(f"  {what}: rel L2 {rel:.3e}, max/RMS {mx:.3e}")
+def assert_output(got, ref: dict, what="", rows=None):
+    rb, rf = ref["out"], ref["out_f64"]
+    if rows is not None:
+        rb, rf = rb[rows], rf[rows]
+    rel, mx, mxr = output_bar(got, rb, rf)
+    say(f"  {what}: rel L2 {rel:.3e} (vs bf16 oracle), max/RMS {mx:.3e} (vs fp64 oracle; {mxr:.3e} vs bf16)")
     assert rel <= 1e-3, f"{what}: relative L2 {rel:.3e} > 1e-3"
     assert mx <= 2e-2, f"{what}: max/RMS {mx:.3e} > 2e-2"
 
@@ -122,5 +134,4 @@ class Layer:
         else:
             self.oracle_experts([0])
         return ffn.moe_ffn(x_vals, s.n_experts, s.top_k, s.n_group, s.topk_group, self.expert, scores=scores,
-                           bias=self.bias, n_shared=s.n_shared, routed_scale=s.routed_scale,
-                           w_router=None if scores is not None else synth.bf16_bits_to_f32(self.wr_bits))
+                           bias=self.bias, n_shared=s.n_shared, routed_scale=s.routed_scale)

@@ -168,6 +168,24 @@ def test_unpermute_weighted_combine():
     assert np.abs(got - round_bf16(ref)).max() <= np.abs(ref).max() * 2.0 ** -7
 
 
+# The gfx950 FP8 MFMA returns each 128-term block sum with a relative error up
+# to ~1.4e-5 of the block's sum of |products| (measured on Gaussian-quantised
+# tiles); allow 5e-5 of sum_k |a_k b_k| per output.
+FP8_MFMA_REL = 5e-5
+
+
+def _absdot(a_q, a_s, gat, b_q, b_s, off):
+    """sum_k |A[m,k] B[n,k]| in fp64 (the scale of the FP8 MFMA's error)."""
+    rows = np.arange(int(off[-1])) if gat is None else gat
+    out = np.zeros((int(off[-1]), b_q.shape[1]))
+    a = np.abs(quant.dequant_1x128(a_q, a_s))
+    for g in range(b_q.shape[0]):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            out[lo:hi] = a[rows[lo:hi]] @ np.abs(quant.dequant_128x128(b_q[g], b_s[g])).T
+    return out
+
+
 def _gemm_case(seed, M_groups, N, K, gather_rows=None):
     r = np.random.default_rng(seed)
     G = len(M_groups)
@@ -203,8 +221,7 @@ def test_grouped_gemm_store_f32(case):
                                            m_max=int(off[-1]))
     ref = gemm.grouped_gemm_blockscaled(a_q, a_s, gat, b_q, b_s, off)
     got = out.cpu().numpy().astype(np.float64)
-    scale = np.abs(ref).max() + 1e-30
-    assert np.abs(got - ref).max() <= 2e-5 * scale, np.abs(got - ref).max() / scale
+    assert np.all(np.abs(got - ref) <= FP8_MFMA_REL * _absdot(a_q, a_s, gat, b_q, b_s, off) + 1e-30)
 
 
 def test_grouped_gemm_bf16_and_scatter():
@@ -226,13 +243,20 @@ def test_grouped_gemm_bf16_and_scatter():
                                            row_weight=to_dev(wt), out_rows=20)
     want = np.zeros((20, N))
     np.add.at(want, dst, wt[:, None].astype(np.float64) * ref)
-    assert np.abs(acc.cpu().numpy() - want).max() <= 2e-5 * np.abs(want).max()
+    bound = np.zeros((20, N))
+    np.add.at(bound, dst, wt[:, None].astype(np.float64) * _absdot(a_q, a_s, None, b_q, b_s, off))
+    assert np.all(np.abs(acc.cpu().numpy() - want) <= FP8_MFMA_REL * bound + 1e-6 * np.abs(want).max())
 
 
-@pytest.mark.parametrize("mg,W,K", [([7, 0, 130], 128, 256), ([64] * 5, 256, 512), ([1000], 128, 384)])
-def test_grouped_gemm_swiglu_quant(mg, W, K):
-    say(f"grouped GEMM SwiGLU+quant groups={mg} W={W} K={K}")
+@pytest.mark.parametrize("mg,W,K,wide", [([7, 0, 130], 128, 256, False), ([64] * 5, 256, 512, False),
+                                         ([1000], 128, 384, False), ([40, 90], 128, 256, True)])
+def test_grouped_gemm_swiglu_quant(mg, W, K, wide):
+    say(f"grouped GEMM SwiGLU+quant groups={mg} W={W} K={K} full-range codes={wide}")
     a_q, a_s, b_q, b_s, off, _ = _gemm_case(W + K, mg, 2 * W, K)
+    if wide:                                   # every finite code, subnormals included, in A
+        r = np.random.default_rng(8)
+        a_q = r.integers(0, 256, a_q.shape).astype(np.uint8)
+        a_q[(a_q & 0x7F) == 0x7F] = 0x01
     h_q, h_s = moe.fp8_grouped_gemm_blockscaled(to_dev(a_q), to_dev(a_s), to_dev(b_q), to_dev(b_s), to_dev(off),
                                                 moe.MOE_EPI_SWIGLU_QUANT, m_max=int(off[-1]))
     gu = gemm.grouped_gemm_blockscaled(a_q, a_s, None, b_q, b_s, off)
@@ -240,11 +264,11 @@ def test_grouped_gemm_swiglu_quant(mg, W, K):
     h = (silu(gu[:, :W]) * gu[:, W:]).astype(np.float32)
     want_q, want_s = quant.quant_1x128(h)
     got_q, got_s = h_q.cpu().numpy(), h_s.cpu().numpy()
-    # fp32 accumulation differs from fp64 by ~1e-6 relative: scales within a few ulps,
-    # codes equal except at rounding midpoints (then one step apart)
-    assert np.allclose(got_s, want_s, rtol=1e-5, atol=0)
+    # exact products, fp32 accumulation (vs fp64): scales within a few ulps, codes equal
+    # except at rounding midpoints (then one step apart)
+    assert np.allclose(got_s, want_s, rtol=2e-6, atol=0)
     mism = got_q != want_q
-    assert mism.mean() <= 2e-3, mism.mean()
+    assert mism.mean() <= 2e-4, mism.mean()
     deq_got = quant.dequant_1x128(got_q, got_s)
     srep = np.repeat(got_s.astype(np.float64), 128, axis=1)
     assert np.all(np.abs(deq_got - h) <= e4m3.half_ulp(np.abs(h) / srep) * srep * 1.01 + 1e-6 * np.abs(h) + 1e-30)
