@@ -65,7 +65,8 @@ class HipEvents:
 
 
 def build_layer(shape, dev):
-    """Device weights of the layer: fp32 draws quantised by fp8_quant_128x128 in place."""
+    """Device weights of the layer: fp32 draws quantised by fp8_quant_128x128, then packed into the
+    GEMMs' fragment order (moe_pack_weights), expert by expert."""
     import torch
 
     import sparse_moe_ffn_sigmoid_amd as moe
@@ -79,16 +80,16 @@ def build_layer(shape, dev):
         kw["w2_q"] = torch.empty((E, d, W), dtype=torch.uint8, device=dev)
         kw["w2_s"] = torch.empty((E, d // 128, W // 128), dtype=torch.float32, device=dev)
         for e in range(E):
-            moe.fp8_quant_128x128(synth.torch_expert_weight(shape, e, "w13", dev), q=kw["w13_q"][e], s=kw["w13_s"][e])
-            moe.fp8_quant_128x128(synth.torch_expert_weight(shape, e, "w2", dev), q=kw["w2_q"][e], s=kw["w2_s"][e])
+            moe.quantize_pack_128x128(synth.torch_expert_weight(shape, e, "w13", dev), q=kw["w13_q"][e], s=kw["w13_s"][e])
+            moe.quantize_pack_128x128(synth.torch_expert_weight(shape, e, "w2", dev), q=kw["w2_q"][e], s=kw["w2_s"][e])
         wr = synth.gen_router_w(shape)
         import numpy as np
         kw["w_router"] = torch.from_numpy(wr.view(np.int16)).to(dev).view(torch.bfloat16)
         if shape.skewed:
             kw["bias"] = torch.from_numpy(synth.skew_bias()).to(dev)
     if shape.n_shared:
-        a, b = moe.fp8_quant_128x128(synth.torch_expert_weight(shape, E, "w13", dev))
-        c, e_ = moe.fp8_quant_128x128(synth.torch_expert_weight(shape, E, "w2", dev))
+        a, b = moe.quantize_pack_128x128(synth.torch_expert_weight(shape, E, "w13", dev))
+        c, e_ = moe.quantize_pack_128x128(synth.torch_expert_weight(shape, E, "w2", dev))
         kw.update(sh_w13_q=a, sh_w13_s=b, sh_w2_q=c, sh_w2_s=e_)
     torch.cuda.synchronize()
     return moe.MoeWeights(**kw)

@@ -89,7 +89,9 @@ typedef struct moe_cfg {
 } moe_cfg_t;
 
 /* Device pointers to one layer's weights.  Expert e's blocks start at
- * e * (its matrix size); scales hold one fp32 per 128x128 block.           */
+ * e * (its matrix size); scales hold one fp32 per 128x128 block.  The e4m3
+ * codes are in MFMA-fragment order (see moe_pack_weights); the shapes below
+ * are the logical row-major [rows][cols] of each matrix.                    */
 typedef struct moe_weights {
   const uint16_t* w_router; /* bf16 [E][hidden]                                     */
   const float* bias;        /* f32 [E] routing-only bias, or NULL (= 0)             */
@@ -128,6 +130,17 @@ MOE_API int fp8_quant_1x128(const void* x, int x_dtype, int rows, int cols, int 
  * over 128x128 blocks ([aguasto] "Quantization": blockwise FP8).
  *   w f32 [rows][cols] -> q e4m3 [rows][cols], s f32 [rows/128][cols/128].   */
 MOE_API int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, void* stream);
+
+/* moe_pack_weights - reorders row-major e4m3 weights [G][N][K] into the
+ * MFMA-fragment order every GEMM of this library reads (offline, like the
+ * 128x128 quantisation; not on the timed path).  Block (g, n16, kb) of 2048
+ * bytes holds rows 16*n16..+15 and columns 128*kb..+127 of matrix g, blocks
+ * ordered by (g, n16, kb), and inside a block byte h*1024 + r*64 + q*16 + b is
+ * B[16*n16 + r][128*kb + 64*h + 16*q + b].  One wave-wide 16-byte load then
+ * reads 1 KB of consecutive bytes, exactly the B operands of a 16x16x128 MFMA,
+ * and a 16-row slice's whole K range is one contiguous stream.  Scales are not
+ * reordered.  N % 16 == 0, K % 128 == 0; src and dst must not overlap.      */
+MOE_API int moe_pack_weights(const uint8_t* src, int G, int N, int K, uint8_t* dst, void* stream);
 
 /* moe_route - gating ([arch blog] "Local Balanced Routing to Experts").
  * Without MOE_ROUTE_SCORES_GIVEN: scores[t][e] = sigmoid(sum_d x[t][d] * w_router[e][d])
@@ -173,7 +186,7 @@ MOE_API int moe_unpermute(const void* y_sorted, int y_dtype, const int32_t* assi
  * ([arch blog] "Fine granularity quantization", "Better Accumulation Precision"):
  *   C[m][n] = sum_kb a_s[row(m)][kb] * b_s[g][n/128][kb] * sum_{k in kb} A[row(m)][k] B[g][n][k]
  *   a_q e4m3 [*][K], a_s f32 [*][K/128]; row(m) = a_gather[m] or m if NULL;
- *   b_q e4m3 [G][N][K], b_s f32 [G][N/128][K/128];
+ *   b_q e4m3 [G][N][K] in MFMA-fragment order (moe_pack_weights), b_s f32 [G][N/128][K/128];
  *   offsets i32 [G+1] (device): group g owns logical rows offsets[g]..offsets[g+1];
  *   M_max: an upper bound of offsets[G] known on the host (sizes the launch).
  *   epilogue MOE_EPI_* with `out` and `epi` as documented at the constants.

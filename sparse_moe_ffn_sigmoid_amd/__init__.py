@@ -6,8 +6,8 @@ and raises MoeError on a non-zero status.  Every step of the layer runs in the
 library's HIP kernels; there is no fallback when the library is missing.
 
 Calls (same names as the C ABI in include/moefp8.h):
-    fp8_quant_1x128, fp8_quant_128x128, moe_route, moe_permute, moe_unpermute,
-    fp8_grouped_gemm_blockscaled, moe_ffn_workspace_size, moe_ffn_forward
+    fp8_quant_1x128, fp8_quant_128x128, moe_pack_weights, moe_route, moe_permute,
+    moe_unpermute, fp8_grouped_gemm_blockscaled, moe_ffn_workspace_size, moe_ffn_forward
 """
 from __future__ import annotations
 
@@ -116,6 +116,23 @@ def fp8_quant_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.T
     s = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=w.device) if s is None else s
     _check("fp8_quant_128x128", _lib.load().fp8_quant_128x128(_p(w), rows, cols, _p(q), _p(s), _stream(w)))
     return q, s
+
+
+def moe_pack_weights(w_q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major e4m3 codes [N, K] or [G, N, K] (uint8) -> the MFMA-fragment order the GEMMs read
+    (same shape and size; see moe_pack_weights in the C header)."""
+    _dev(w_q, "w_q")
+    G, N, K = (1, *w_q.shape) if w_q.dim() == 2 else tuple(w_q.shape)
+    out = torch.empty_like(w_q) if out is None else out
+    _check("moe_pack_weights", _lib.load().moe_pack_weights(_p(w_q), G, N, K, _p(out), _stream(w_q)))
+    return out
+
+
+def quantize_pack_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+    """fp32 weights [N, K] -> (packed e4m3 codes [N, K], scales [N/128, K/128]): fp8_quant_128x128
+    followed by moe_pack_weights (a temporary holds the row-major codes)."""
+    rm, s = fp8_quant_128x128(w, s=s)
+    return moe_pack_weights(rm, out=q), s
 
 
 def moe_route(cfg: MoeConfig, T: int, device, scores: torch.Tensor | None = None, x: torch.Tensor | None = None,

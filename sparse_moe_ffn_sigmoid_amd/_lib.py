@@ -20,7 +20,7 @@ MOE_EPI_STORE_F32, MOE_EPI_STORE_BF16, MOE_EPI_SWIGLU_QUANT, MOE_EPI_WEIGHTED_SC
 
 EXPORTED = ("moe_status_string", "moe_last_error", "fp8_quant_1x128", "fp8_quant_128x128", "moe_route",
             "moe_permute_workspace_size", "moe_permute", "moe_unpermute", "fp8_grouped_gemm_blockscaled",
-            "moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_stages")
+            "moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_stages", "moe_pack_weights")
 MOE_FWD_STAGE_EVENTS = 6
 
 
@@ -58,6 +58,7 @@ def load() -> ctypes.CDLL:
         "moe_last_error": (ctypes.c_char_p, []),
         "fp8_quant_1x128": (i, [vp, i, i, i, i, vp, i, vp, vp]),
         "fp8_quant_128x128": (i, [vp, i, i, vp, vp, vp]),
+        "moe_pack_weights": (i, [vp, i, i, i, vp, vp]),
         "moe_route": (i, [vp, vp, vp, i, ctypes.POINTER(MoeCfgC), vp, i, vp, vp, vp]),
         "moe_permute_workspace_size": (sz, [i, i, i]),
         "moe_permute": (i, [vp, i, i, i, vp, vp, vp, vp, i, vp, vp, sz, vp]),

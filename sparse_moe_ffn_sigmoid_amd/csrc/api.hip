@@ -297,6 +297,16 @@ int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int
   return ok();
 }
 
+int moe_pack_weights(const uint8_t* src, int G, int N, int K, uint8_t* dst, void* stream) {
+  REQUIRE(G >= 0 && N >= 0 && K >= 0, MOE_ERR_INVALID_ARG, "negative size");
+  REQUIRE(N % 16 == 0 && K % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "N %d %% 16 or K %d %% 128 != 0", N, K);
+  if ((long)G * N * K == 0) return ok();
+  REQUIRE(src && dst && src != dst, MOE_ERR_INVALID_ARG, "NULL or aliased pointers");
+  REQUIRE(aligned(src, 16) && aligned(dst, 16), MOE_ERR_INVALID_ARG, "pointer not 16-byte aligned");
+  HIP_TRY(launch_pack(src, G, N, K, dst, (hipStream_t)stream), "moe_pack_weights");
+  return ok();
+}
+
 size_t moe_ffn_workspace_size(int T, const moe_cfg_t* cfg) {
   if (T < 0 || check_layer_cfg(cfg) != MOE_OK) return 0;
   return fwd_layout(T, cfg).total;

@@ -38,6 +38,69 @@ namespace moefp8 {
 
 __device__ __forceinline__ int swz(int r, int c) { return (r << 7) + ((c ^ (r & 7)) << 4); }
 
+// Maps blockIdx.x to (segment, group, first row, end row) for tiles of bm
+// rows.  Static segment tiles come first; for the dynamic segment the
+// workgroup scans the groups' tile counts (offsets read on the device) in LDS.
+// Returns false (uniformly) for workgroups past the real tile count.
+__device__ bool find_tile(const GemmArgs& args, int bm, int* scan_tmp, int* pre, int* pick, int& si, int& g, int& m0,
+                          int& m_end) {
+  const int tid = threadIdx.x;
+  int v = blockIdx.x;
+  if (v < args.seg[0].m_tiles) {
+    si = 0;
+    g = 0;
+    m0 = v * bm;
+    m_end = args.seg[0].m_rows;
+    return true;
+  }
+  v -= args.seg[0].m_tiles;
+  const GemmSeg& sd = args.seg[1];
+  if (v >= sd.m_tiles) return false;
+  const int G = sd.G;
+  const int per = (G + 255) >> 8;               // groups per thread (G <= 1024)
+  int cnt[4];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gi = tid * per + i;
+    cnt[i] = 0;
+    if (i < per && gi < G) cnt[i] = (sd.offsets[gi + 1] - sd.offsets[gi] + bm - 1) / bm;
+    local += cnt[i];
+  }
+  scan_tmp[tid] = local;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int add = tid >= o ? scan_tmp[tid - o] : 0;
+    __syncthreads();
+    scan_tmp[tid] += add;
+    __syncthreads();
+  }
+  int run = scan_tmp[tid] - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gi = tid * per + i;
+    run += cnt[i];
+    if (i < per && gi < G) pre[gi] = run;       // inclusive prefix
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int lo = 0, hi = G;                           // first group with pre[g] > v
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] > v) hi = mid; else lo = mid + 1;
+    }
+    pick[0] = lo;
+  }
+  __syncthreads();
+  g = pick[0];
+  if (g >= G) return false;
+  si = 1;
+  const int tiles_g = (sd.offsets[g + 1] - sd.offsets[g] + bm - 1) / bm;
+  m0 = sd.offsets[g] + (v - (pre[g] - tiles_g)) * bm;
+  m_end = sd.offsets[g + 1];
+  return true;
+}
+
 template <int BM, int NB>
 struct Tile {
   static constexpr int kA = BM * 128;            // A codes of one K block
@@ -64,61 +127,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
   __shared__ float red[4][BM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
-  int v = blockIdx.x;
   const int nt = blockIdx.y;
   int si, g, m0, m_end;
-  if (v < args.seg[0].m_tiles) {
-    si = 0;
-    g = 0;
-    m0 = v * BM;
-    m_end = args.seg[0].m_rows;
-  } else {
-    v -= args.seg[0].m_tiles;
-    const GemmSeg& sd = args.seg[1];
-    if (v >= sd.m_tiles) return;
-    const int G = sd.G;
-    const int per = (G + 255) >> 8;           // groups per thread (G <= 1024)
-    int cnt[4];
-    int local = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gi = tid * per + i;
-      cnt[i] = 0;
-      if (i < per && gi < G) cnt[i] = (sd.offsets[gi + 1] - sd.offsets[gi] + BM - 1) / BM;
-      local += cnt[i];
-    }
-    scan_tmp[tid] = local;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      const int add = tid >= o ? scan_tmp[tid - o] : 0;
-      __syncthreads();
-      scan_tmp[tid] += add;
-      __syncthreads();
-    }
-    int run = scan_tmp[tid] - local;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gi = tid * per + i;
-      run += cnt[i];
-      if (i < per && gi < G) pre[gi] = run;   // inclusive prefix
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int lo = 0, hi = G;                       // first group with pre[g] > v
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] > v) hi = mid; else lo = mid + 1;
-      }
-      pick[0] = lo;
-    }
-    __syncthreads();
-    g = pick[0];
-    if (g >= G) return;                         // past the real tile count
-    si = 1;
-    const int tiles_g = (sd.offsets[g + 1] - sd.offsets[g] + BM - 1) / BM;
-    m0 = sd.offsets[g] + (v - (pre[g] - tiles_g)) * BM;
-    m_end = sd.offsets[g + 1];
-  }
+  if (!find_tile(args, BM, scan_tmp, pre, pick, si, g, m0, m_end)) return;
   // this tile's segment, field by field (kept in scalar registers)
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& s1 = args.seg[1];
@@ -143,15 +154,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
     a_src[i] = a_q + src * K + ((ci & 7) << 4);
     a_dst[i] = swz(r, ci & 7);
   }
+  // B is in MFMA-fragment order: the tile's K block is NB x 8 contiguous 2 KB
+  // blocks (16 rows each); LDS keeps that order, so fragment reads are 1 KB
+  // contiguous per wave instruction (no bank conflicts, no swizzle needed).
   const uint8_t* b_src[B_PER];
   int b_dst[B_PER];
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
     const int ci = tid + 256 * i;
-    const int rb = ci >> 3;
-    const int brow = (rb >> 7) * half + nt * 128 + (rb & 127);
-    b_src[i] = bq + (long)brow * K + ((ci & 7) << 4);
-    b_dst[i] = TL::kA + swz(rb, ci & 7);
+    const int blk = ci >> 7;                      // local 16-row block: nb * 8 + n16
+    const int n16 = ((blk >> 3) * half + nt * 128) / 16 + (blk & 7);
+    b_src[i] = bq + (long)n16 * nkb * 2048 + ((ci & 127) << 4);
+    b_dst[i] = TL::kA + (ci << 4);
   }
   // thread tid < BM stages a_s of row tid; threads BM .. BM+NB-1 stage b_s of block tid-BM
   const float* s_src = nullptr;
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
     _Pragma("unroll") for (int i = 0; i < A_PER; ++i) ra[i] =                               \
         *reinterpret_cast<const u32x4*>(a_src[i] + ko_);                                     \
     _Pragma("unroll") for (int i = 0; i < B_PER; ++i) rb[i] =                               \
-        *reinterpret_cast<const u32x4*>(b_src[i] + ko_);                                     \
+        *reinterpret_cast<const u32x4*>(b_src[i] + (long)(kb_) * 2048);                      \
     if (s_src) rs = s_src[kb_];                                                              \
   }
 #define GEMM_SSTORE(buf_)                                                                    \
@@ -210,9 +224,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
     }
 #pragma unroll
     for (int nj = 0; nj < NT; ++nj) {
-      const int r = (nj >> 1) * 128 + wave * 32 + (nj & 1) * 16 + r16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + TL::kA + swz(r, q));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + TL::kA + swz(r, q + 4));
+      const int blk = (nj >> 1) * 8 + wave * 2 + (nj & 1);
+      const uint8_t* fb = st + TL::kA + blk * 2048 + r16 * 64 + q * 16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(fb);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(fb + 1024);
       bf[nj] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
     const float* sa = reinterpret_cast<const float*>(st + TL::kA + TL::kB);
@@ -335,6 +350,216 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming variant for groups of at most 16 rows (decode-sized
+// batches).  Each B byte is used by exactly one wave, so B bypasses LDS: every
+// lane loads its own MFMA fragments straight from HBM (fragment-ordered
+// weights: two 1 KB contiguous wave loads per 16 rows and K block, and a wave's
+// whole stream over K is one contiguous range), with P K blocks of loads in
+// flight per wave; the waves never synchronise inside the K loop.  A (the <= 16 activation rows) comes from L2
+// the same way.  Wave w covers NTW 16-column tiles of each of the NB B blocks;
+// with NB = 2 (gate/up) a workgroup covers 128 h columns, the SwiGLU
+// requantisation tile.
+template <int NB, int NTW, int P, int EPI>
+__global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
+  constexpr int NF = NB * NTW;                 // B fragments per lane per K block
+  constexpr int CW = 16 * NTW;                 // columns per wave in each B block
+  constexpr bool kExact = EPI == kEpiSwiglu;
+  __shared__ int scan_tmp[256];
+  __shared__ int pre[1024];
+  __shared__ int pick[1];
+  __shared__ float red[4][16];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[16 * 128];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
+  int si, g, m0, m_end;
+  if (!find_tile(args, 16, scan_tmp, pre, pick, si, g, m0, m_end)) return;
+  const GemmSeg& s0 = args.seg[0];
+  const GemmSeg& s1 = args.seg[1];
+  const int K = si ? s1.K : s0.K, nkb = K >> 7;
+  const int half = (si ? s1.N : s0.N) / NB;
+  const int nbase = blockIdx.y * 4 * CW;        // first column of this workgroup in each block
+  if (nbase >= half) return;
+  const int ncol0 = nbase + wave * CW;         // first column of this wave in each block
+  const bool wave_live = ncol0 < half;          // all waves live when half % (4 CW) == 0
+  const uint8_t* const a_q = si ? s1.a_q : s0.a_q;
+  const float* const a_s = si ? s1.a_s : s0.a_s;
+  const int32_t* const gat = si ? s1.a_gather : s0.a_gather;
+  const uint8_t* const bq = (si ? s1.b_q : s0.b_q) + (long long)g * (si ? s1.b_stride : s0.b_stride);
+  const float* const bs = (si ? s1.b_s : s0.b_s) + (long long)g * (si ? s1.bs_stride : s0.bs_stride);
+
+  const int my_m = m0 + r16 < m_end ? m0 + r16 : m0;
+  const long src = gat ? (long)gat[my_m] : (long)my_m;
+  const uint8_t* a_ptr = a_q + src * K + 16 * q;
+  const float* sa_ptr = a_s + src * nkb;
+  const uint8_t* b_ptr[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int nb = f / NTW, j = f % NTW;
+    const int n16 = wave_live ? (nb * half + ncol0) / 16 + j : 0;
+    b_ptr[f] = bq + (long)n16 * nkb * 2048 + r16 * 64 + q * 16;   // MFMA-fragment order: 1 KB per wave load
+  }
+  const float* sb_ptr[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) sb_ptr[nb] = bs + (long)((nb * half + (wave_live ? ncol0 : 0)) >> 7) * nkb;
+
+  u32x4 al[P], ah[P], bl[P][NF], bh[P][NF];
+  float sav[P], sbv[P][NB];
+#define STREAM_LOAD(p_, kb_)                                                                 \
+  {                                                                                          \
+    const int ko_ = (kb_) << 7;                                                              \
+    al[p_] = *reinterpret_cast<const u32x4*>(a_ptr + ko_);                                   \
+    ah[p_] = *reinterpret_cast<const u32x4*>(a_ptr + ko_ + 64);                              \
+    _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                        \
+      bl[p_][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_ptr[f] + (long)(kb_) * 2048));        \
+      bh[p_][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_ptr[f] + (long)(kb_) * 2048 + 1024)); \
+    }                                                                                        \
+    sav[p_] = sa_ptr[kb_];                                                                   \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) sbv[p_][nb] = sb_ptr[nb][kb_];        \
+  }
+
+  v4f acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (wave_live) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (p < nkb) STREAM_LOAD(p, p);
+    for (int kb0 = 0; kb0 < nkb; kb0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int kb = kb0 + p;
+        if (kb < nkb) {
+          const v8i af = v8i{(int)al[p].x, (int)al[p].y, (int)al[p].z, (int)al[p].w,
+                             (int)ah[p].x, (int)ah[p].y, (int)ah[p].z, (int)ah[p].w};
+          v4f part[NF];
+          if constexpr (kExact) {
+            v8bf ab[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ab[j] = e4m3x8_to_bf16((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1]);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                  (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+              v4f t = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    ab[j], e4m3x8_to_bf16((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1]), t, 0, 0, 0);
+              part[f] = t;
+            }
+          } else {
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                  (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+              part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                         0, 0, 0);
+            }
+          }
+          // row 4q+i's activation scale sits in lane 4q+i
+          float srow[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) srow[i] = __shfl(sav[p], 4 * q + i);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const float sbf = sbv[p][f / NTW];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[f][i] = fmaf(part[f][i], srow[i] * sbf, acc[f][i]);
+          }
+          if (kb + P < nkb) STREAM_LOAD(p, kb + P);
+        }
+      }
+    }
+  }
+#undef STREAM_LOAD
+
+  void* const out = si ? s1.out : s0.out;
+  float* const out_s = si ? s1.out_s : s0.out_s;
+  const int ld_out = si ? s1.ld_out : s0.ld_out;
+  const int32_t* const dst_row = si ? s1.dst_row : s0.dst_row;
+  const float* const row_w = si ? s1.row_w : s0.row_w;
+  // lane holds rows m0 + 4q + i, columns ncol0 + 16 j + r16 of each B block
+  if constexpr (EPI == kEpiSwiglu) {
+    float h[NTW][4];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[j][i] = swiglu(acc[j][i], acc[NTW + j][i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) mx = fmaxf(mx, fabsf(h[j][i]));
+      mx = group_max<16>(mx);
+      if (r16 == 0) red[wave][4 * q + i] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q + i;
+      const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+      const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) stage[r * 128 + wave * CW + 16 * j + r16] = (uint8_t)e4m3_encode(h[j][i] / sc);
+      if (wave == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + (nbase >> 7)] = sc;
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const int r = tid >> 3, c = tid & 7;
+      if (m0 + r < m_end)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(out) + (long)(m0 + r) * ld_out + nbase + c * 16) =
+            *reinterpret_cast<const u32x4*>(stage + r * 128 + c * 16);
+    }
+  } else {
+    if (!wave_live) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 4 * q + i;
+      if (m >= m_end) continue;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int n = ncol0 + 16 * f + r16;
+        const float val = acc[f][i];
+        if constexpr (EPI == kEpiF32) {
+          reinterpret_cast<float*>(out)[(long)m * ld_out + n] = val;
+        } else if constexpr (EPI == kEpiBf16) {
+          reinterpret_cast<uint16_t*>(out)[(long)m * ld_out + n] = f32_to_bf16_rne(val);
+        } else {
+          const long dst = dst_row ? (long)dst_row[m] : (long)m;
+          const float wgt = row_w ? row_w[m] : 1.0f;
+          atomicAdd(reinterpret_cast<float*>(out) + dst * ld_out + n, wgt * val);
+        }
+      }
+    }
+  }
+}
+
+static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
+  const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
+  if (mt == 0) return hipSuccess;
+  const bool swiglu = epi == kEpiSwiglu;
+  const int cols = swiglu ? 4 * 16 * 2 : 4 * 16 * 4;         // columns per workgroup in each block
+  int ny = 0;
+  for (int s = 0; s < 2; ++s) {
+    const GemmSeg& S = args.seg[s];
+    if (S.m_tiles > 0) {
+      const int half = S.N / (swiglu ? 2 : 1);
+      const int n = (half + cols - 1) / cols;
+      ny = ny > n ? ny : n;
+    }
+  }
+  if (ny == 0) return hipSuccess;
+  const dim3 grid(mt, ny);
+  switch (epi) {
+    case kEpiSwiglu: stream_gemm_kernel<2, 2, 4, kEpiSwiglu><<<grid, 256, 0, st>>>(args); break;
+    case kEpiF32: stream_gemm_kernel<1, 4, 4, kEpiF32><<<grid, 256, 0, st>>>(args); break;
+    case kEpiBf16: stream_gemm_kernel<1, 4, 4, kEpiBf16><<<grid, 256, 0, st>>>(args); break;
+    default: stream_gemm_kernel<1, 4, 4, kEpiScatter><<<grid, 256, 0, st>>>(args); break;
+  }
+  return hipGetLastError();
+}
+
 template <int BM>
 static hipError_t launch_bm(const GemmArgs& args, int epi, hipStream_t st) {
   const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
@@ -358,7 +583,7 @@ static hipError_t launch_bm(const GemmArgs& args, int epi, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st) {
   switch (bm) {
-    case 16: return launch_bm<16>(args, epi, st);
+    case 16: return launch_stream(args, epi, st);
     case 32: return launch_bm<32>(args, epi, st);
     case 64: return launch_bm<64>(args, epi, st);
     default: return launch_bm<128>(args, epi, st);

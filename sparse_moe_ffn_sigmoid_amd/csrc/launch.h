@@ -16,7 +16,7 @@ struct GemmSeg {
   const uint8_t* a_q;        // [*][K] e4m3
   const float* a_s;          // [*][K/128]
   const int32_t* a_gather;   // logical row -> source row, or nullptr
-  const uint8_t* b_q;        // [G][N][K]
+  const uint8_t* b_q;        // [G][N][K] in MFMA-fragment order (moe_pack_weights)
   const float* b_s;          // [G][N/128][K/128]
   long long b_stride;        // N*K
   long long bs_stride;       // (N/128)*(K/128)
@@ -40,6 +40,7 @@ struct GemmArgs {
 hipError_t launch_quant_1x128(const void* x, bool bf16, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
                               hipStream_t st);
 hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_pack(const uint8_t* src, int G, int N, int K, uint8_t* dst, hipStream_t st);
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, hipStream_t st);
 hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,
                         float routed_scale, int32_t* topk_idx, float* topk_w, hipStream_t st);

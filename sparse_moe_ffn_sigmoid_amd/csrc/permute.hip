@@ -111,6 +111,81 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   }
 }
 
+// Small batches (n <= kSmallN, E <= kSmallE): the whole counting sort in one
+// workgroup of 1024 threads (16 waves): LDS histogram, block scan into the
+// offsets, then per 1024-assignment chunk: ballot ranks inside each wave, a
+// prefix over the 16 waves per expert, positions = running base + prefix + rank.
+constexpr int kSmallN = 8192;
+constexpr int kSmallE = 512;
+
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restrict__ idx, int n, int k, int E,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_assign,
+                                                          int32_t* __restrict__ assign_pos,
+                                                          int32_t* __restrict__ sorted_token,
+                                                          const float* __restrict__ topk_w,
+                                                          float* __restrict__ sorted_w) {
+  __shared__ int base[kSmallE];
+  __shared__ int wcnt[16][kSmallE];
+  __shared__ int scan[1024];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += 1024) base[e] = 0;
+  __syncthreads();
+  for (int a = tid; a < n; a += 1024) atomicAdd(&base[idx[a]], 1);
+  __syncthreads();
+  const int cnt = tid < E ? base[tid] : 0;
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    base[tid] = scan[tid] - cnt;                    // exclusive prefix: first sorted row of expert tid
+    offsets[tid] = scan[tid] - cnt;
+  }
+  if (tid == 0) offsets[E] = n;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    for (int i = tid; i < 16 * E; i += 1024) wcnt[i / E][i % E] = 0;
+    __syncthreads();
+    const int a = c0 + tid;
+    const bool valid = a < n;
+    const int e = valid ? idx[a] : E;
+    unsigned long long peers = ~0ull;
+    for (int bit = 0; bit < nbits; ++bit) {
+      const unsigned long long m = __ballot((e >> bit) & 1);
+      peers &= ((e >> bit) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    const int gsize = __popcll(peers);
+    if (valid && rank == gsize - 1) wcnt[wave][e] = gsize;
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += 1024) {
+      int run = base[ee];
+      for (int w = 0; w < 16; ++w) {
+        const int v = wcnt[w][ee];
+        wcnt[w][ee] = run;
+        run += v;
+      }
+      base[ee] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      const int pos = wcnt[wave][e] + rank;
+      sorted_assign[pos] = a;
+      assign_pos[a] = pos;
+      if (sorted_token) sorted_token[pos] = a / k;
+      if (sorted_w) sorted_w[pos] = topk_w[a];
+    }
+    __syncthreads();
+  }
+}
+
 // rows_out[p] = rows_in[sorted_assign[p] / k], row_bytes % 16 == 0.
 __global__ __launch_bounds__(256) void perm_gather_kernel(const uint4* __restrict__ rows_in, int row_vec, int n, int k,
                                                           const int32_t* __restrict__ sorted_assign,
@@ -189,6 +264,11 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
                           int32_t* assign_pos, int32_t* sorted_token, const float* topk_w, float* sorted_w,
                           int32_t* scratch, hipStream_t st) {
   const int n = T * k;
+  if (n <= kSmallN && E <= kSmallE) {
+    perm_small_kernel<<<1, 1024, 0, st>>>(idx, n, k, E, offsets, sorted_assign, assign_pos, sorted_token, topk_w,
+                                          sorted_w);
+    return hipGetLastError();
+  }
   const int nchunks = (n + kChunk - 1) / kChunk;
   if (nchunks > 0) perm_count_kernel<<<nchunks, 256, E * sizeof(int), st>>>(idx, n, E, scratch);
   perm_scan_kernel<<<1, 1024, 0, st>>>(scratch, nchunks, E, offsets);

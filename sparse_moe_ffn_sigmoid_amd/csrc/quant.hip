@@ -98,6 +98,33 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
   if (tid == 0) s[br * (cols >> 7) + bc] = sc;
 }
 
+// Row-major e4m3 [G][N][K] -> MFMA-fragment order.  Block (g, n16, kb) holds
+// rows 16 n16 .. +15, columns 128 kb .. +127 in 2 KB: byte
+// (h * 1024 + r * 64 + q * 16 + b) = B[16 n16 + r][128 kb + 64 h + 16 q + b], so
+// the lane (r, q) of a 16x16x128 MFMA fragment finds its two 16-byte pieces at
+// h = 0 and h = 1, and one wave-wide load covers 1 KB of consecutive bytes.
+__global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ src, long nchunks, int N, int K,
+                                                   uint4* __restrict__ dst) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;   // destination 16-byte chunk
+  if (i >= nchunks) return;
+  const int nkb = K >> 7;
+  const long blk = i >> 7;                                // 2 KB block index (g, n16, kb)
+  const int w = (int)(i & 127);
+  const int h = w >> 6, r = (w >> 2) & 15, q = w & 3;
+  const int kb = (int)(blk % nkb);
+  const long gn16 = blk / nkb;                            // g * (N/16) + n16
+  const long row = gn16 * 16 + r;                         // g * N + n
+  dst[i] = src[(row * K + kb * 128 + 64 * h + 16 * q) >> 4];
+}
+
+hipError_t launch_pack(const uint8_t* src, int G, int N, int K, uint8_t* dst, hipStream_t st) {
+  const long nchunks = (long)G * N * K / 16;
+  if (nchunks == 0) return hipSuccess;
+  pack_kernel<<<(unsigned)((nchunks + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint4*>(src), nchunks, N, K,
+                                                                  reinterpret_cast<uint4*>(dst));
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_1x128(const void* x, bool bf16, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
                               hipStream_t st) {
   const long ntiles = (long)rows * (cols / 128);

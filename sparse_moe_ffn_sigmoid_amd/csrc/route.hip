@@ -46,7 +46,133 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict_
   }
 }
 
-// One wave per token.  Biased scores live in LDS; lane g < n_group scores
+// Small batches: one workgroup per 16 tokens x 16 experts, its 4 waves split
+// the hidden dimension in quarters (8 MFMA steps in flight per wave) and add
+// their partial logits through LDS; enough workgroups to spread the 3.7 MB of
+// router weights over many CUs even at T = 64.
+__global__ __launch_bounds__(256) void router_splitk_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ w, int T, int E, int D,
+                                                            float* __restrict__ scores) {
+  __shared__ v4f part[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int ta = min(t0 + r16, T - 1);
+  const int kq = D >> 2;                        // D % 128 == 0: quarters are multiples of 32
+  const uint16_t* xa = x + (long)ta * D + wave * kq + 8 * q;
+  const uint16_t* wb = w + (long)(e0 + r16) * D + wave * kq + 8 * q;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 256 <= kq; k += 256) {
+    v8bf a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = *reinterpret_cast<const v8bf*>(xa + k + 32 * u);
+      b[u] = *reinterpret_cast<const v8bf*>(wb + k + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+  }
+  for (; k < kq; k += 32) {
+    const v8bf a = *reinterpret_cast<const v8bf*>(xa + k);
+    const v8bf b = *reinterpret_cast<const v8bf*>(wb + k);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    const v4f t = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = t0 + 4 * q + i;
+      if (tt < T) scores[(long)tt * E + e0 + r16] = 1.0f / (1.0f + expf(-t[i]));
+    }
+  }
+}
+
+// Register-resident routing for the common layouts: lane l holds experts
+// l*EPL .. l*EPL+EPL-1 (EPL = E/64, or 1 when E <= 64), a group is LPG
+// consecutive lanes.  Group top-2 merges pairs across the group's lanes with
+// xor shuffles; the top_k rounds are wave-wide argmaxes (ties to the lower id).
+template <int EPL>
+__global__ __launch_bounds__(256) void route_reg_kernel(const float* __restrict__ scores,
+                                                        const float* __restrict__ bias, int T, int E, int k, int G,
+                                                        int gk, int rule, float routed_scale,
+                                                        int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;                               // whole wave: no block-level barrier below
+  const float* s = scores + (long)t * E;
+  const int e0 = lane * EPL;
+  const bool live = e0 < E;
+  float sv[EPL], b[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    sv[i] = live ? s[e0 + i] : 0.0f;
+    b[i] = live ? sv[i] + (bias ? bias[e0 + i] : 0.0f) : -INFINITY;
+  }
+  const int gsz = E / G;
+  const int lpg = gsz / EPL;                        // lanes per group (a power of two here)
+  float t1 = b[0], t2 = -INFINITY;
+#pragma unroll
+  for (int i = 1; i < EPL; ++i) {
+    if (b[i] > t1) {
+      t2 = t1;
+      t1 = b[i];
+    } else if (b[i] > t2) {
+      t2 = b[i];
+    }
+  }
+  for (int o = 1; o < lpg; o <<= 1) {               // merge the two largest of two multisets
+    const float u1 = __shfl_xor(t1, o), u2 = __shfl_xor(t2, o);
+    const float hi = fmaxf(t1, u1), lo = fminf(t1, u1);
+    t2 = fmaxf(lo, fmaxf(t2, u2));
+    t1 = hi;
+  }
+  const float gscore = (rule == 1 || gsz == 1) ? t1 : t1 + t2;
+  const int mygroup = lane / lpg;
+  int rank = 0;
+  for (int g = 0; g < G; ++g) {
+    const float o = __shfl(gscore, g * lpg);
+    rank += (o > gscore || (o == gscore && g < mygroup)) ? 1 : 0;
+  }
+  const bool kept = live && rank < gk;
+  unsigned taken = 0;
+  int mine = 0;
+  for (int j = 0; j < k; ++j) {
+    float best = -INFINITY;
+    int bi = INT_MAX;
+    if (kept) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        if (!((taken >> i) & 1u) && (b[i] > best || bi == INT_MAX)) {
+          best = b[i];
+          bi = e0 + i;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > best || (ov == best && oi < bi)) {
+        best = ov;
+        bi = oi;
+      }
+    }
+    if (bi == INT_MAX) bi = 0;                      // only with NaN scores, outside the contract
+    if (bi >= e0 && bi < e0 + EPL) taken |= 1u << (bi - e0);
+    if (lane == j) mine = bi;
+  }
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) sum += s[__shfl(mine, j)];
+  if (lane < k) {
+    topk_idx[(long)t * k + lane] = mine;
+    topk_w[(long)t * k + lane] = (s[mine] / sum) * routed_scale;
+  }
+}
+
+// General layouts (any E <= 1024 and group size): one wave per token.  Biased scores live in LDS; lane g < n_group scores
 // group g; groups are ranked with ties to the lower index; then top_k rounds
 // of a wave-wide argmax (ties to the lower expert id) over the kept groups.
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
@@ -120,7 +246,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const unsigned gx = (unsigned)((T + 63) / 64);
-  if (E % 64 == 0 && T > 256) {
+  if (T <= 512) {
+    router_splitk_kernel<<<dim3((T + 15) / 16, E / 16), 256, 0, st>>>(x, w, T, E, D, scores);
+  } else if (E % 64 == 0) {
     router_kernel<4><<<dim3(gx, E / 64), 256, 0, st>>>(x, w, T, E, D, scores);
   } else {
     router_kernel<1><<<dim3(gx, E / 16), 256, 0, st>>>(x, w, T, E, D, scores);
@@ -131,8 +259,22 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int
 hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,
                         float routed_scale, int32_t* topk_idx, float* topk_w, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  route_kernel<<<(T + 3) / 4, 256, 4 * E * sizeof(float), st>>>(scores, bias, T, E, k, G, gk, rule, routed_scale,
-                                                                topk_idx, topk_w);
+  const unsigned grid = (unsigned)((T + 3) / 4);
+  const int epl = E <= 64 ? 1 : E / 64;
+  const bool reg_layout = (E <= 64 || E % 64 == 0) && (E / G) % epl == 0;
+  const int lpg = reg_layout ? (E / G) / epl : 0;
+  if (reg_layout && (lpg & (lpg - 1)) == 0 && (epl == 1 || epl == 2 || epl == 4 || epl == 8 || epl == 16)) {
+    switch (epl) {
+      case 1: route_reg_kernel<1><<<grid, 256, 0, st>>>(scores, bias, T, E, k, G, gk, rule, routed_scale, topk_idx, topk_w); break;
+      case 2: route_reg_kernel<2><<<grid, 256, 0, st>>>(scores, bias, T, E, k, G, gk, rule, routed_scale, topk_idx, topk_w); break;
+      case 4: route_reg_kernel<4><<<grid, 256, 0, st>>>(scores, bias, T, E, k, G, gk, rule, routed_scale, topk_idx, topk_w); break;
+      case 8: route_reg_kernel<8><<<grid, 256, 0, st>>>(scores, bias, T, E, k, G, gk, rule, routed_scale, topk_idx, topk_w); break;
+      default: route_reg_kernel<16><<<grid, 256, 0, st>>>(scores, bias, T, E, k, G, gk, rule, routed_scale, topk_idx, topk_w); break;
+    }
+  } else {
+    route_kernel<<<grid, 256, 4 * E * sizeof(float), st>>>(scores, bias, T, E, k, G, gk, rule, routed_scale,
+                                                           topk_idx, topk_w);
+  }
   return hipGetLastError();
 }
 

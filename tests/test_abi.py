@@ -101,6 +101,12 @@ def test_route_needs_router_weights_without_given_scores(lib):
     assert lib.moe_route(FAKE, FAKE, None, 4, ctypes.byref(c), FAKE, 8, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
 
 
+def test_pack_checks(lib):
+    assert lib.moe_pack_weights(FAKE, 1, 24, 128, ctypes.c_void_p(0x20000), None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert lib.moe_pack_weights(FAKE, 1, 16, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG      # aliased
+    assert lib.moe_pack_weights(None, 0, 16, 128, None, None) == _lib.MOE_OK                   # empty
+
+
 def test_permute_checks(lib):
     assert lib.moe_permute(FAKE, 4, 2, 2000, FAKE, FAKE, FAKE, None, 0, None, FAKE, 1 << 20, None) == \
         _lib.MOE_ERR_UNSUPPORTED_SHAPE

@@ -186,6 +186,22 @@ def _absdot(a_q, a_s, gat, b_q, b_s, off):
     return out
 
 
+def _packed(b_q):
+    """Row-major codes [G, N, K] -> device tensor in the GEMMs' fragment order."""
+    return moe.moe_pack_weights(to_dev(b_q))
+
+
+def test_pack_weights_layout():
+    say("moe_pack_weights layout")
+    r = np.random.default_rng(12)
+    G, N, K = 3, 48, 384
+    src = r.integers(0, 256, (G, N, K), dtype=np.uint8)
+    got = moe.moe_pack_weights(to_dev(src)).cpu().numpy().reshape(-1)
+    # block (g, n16, kb) of 2048 bytes; byte h*1024 + r*64 + q*16 + b = B[16 n16 + r][128 kb + 64 h + 16 q + b]
+    want = src.reshape(G, N // 16, 16, K // 128, 2, 4, 16).transpose(0, 1, 3, 4, 2, 5, 6).reshape(-1)
+    assert np.array_equal(got, want)
+
+
 def _gemm_case(seed, M_groups, N, K, gather_rows=None):
     r = np.random.default_rng(seed)
     G = len(M_groups)
@@ -216,7 +232,7 @@ def test_grouped_gemm_store_f32(case):
     mg, N, K, gr = case
     say(f"grouped GEMM f32 groups={mg[:8]} N={N} K={K} gather={gr}")
     a_q, a_s, b_q, b_s, off, gat = _gemm_case(len(mg) + N, mg, N, K, gr)
-    out = moe.fp8_grouped_gemm_blockscaled(to_dev(a_q), to_dev(a_s), to_dev(b_q), to_dev(b_s), to_dev(off),
+    out = moe.fp8_grouped_gemm_blockscaled(to_dev(a_q), to_dev(a_s), _packed(b_q), to_dev(b_s), to_dev(off),
                                            moe.MOE_EPI_STORE_F32, a_gather=None if gat is None else to_dev(gat),
                                            m_max=int(off[-1]))
     ref = gemm.grouped_gemm_blockscaled(a_q, a_s, gat, b_q, b_s, off)
@@ -229,7 +245,7 @@ def test_grouped_gemm_bf16_and_scatter():
     mg = [5, 0, 70, 33]
     N, K = 256, 256
     a_q, a_s, b_q, b_s, off, _ = _gemm_case(77, mg, N, K)
-    args = [to_dev(a_q), to_dev(a_s), to_dev(b_q), to_dev(b_s), to_dev(off)]
+    args = [to_dev(a_q), to_dev(a_s), _packed(b_q), to_dev(b_s), to_dev(off)]
     ref = gemm.grouped_gemm_blockscaled(a_q, a_s, None, b_q, b_s, off)
     out = moe.fp8_grouped_gemm_blockscaled(*args, moe.MOE_EPI_STORE_BF16, m_max=int(off[-1]))
     from oracle.ffn import round_bf16
@@ -257,7 +273,7 @@ def test_grouped_gemm_swiglu_quant(mg, W, K, wide):
         r = np.random.default_rng(8)
         a_q = r.integers(0, 256, a_q.shape).astype(np.uint8)
         a_q[(a_q & 0x7F) == 0x7F] = 0x01
-    h_q, h_s = moe.fp8_grouped_gemm_blockscaled(to_dev(a_q), to_dev(a_s), to_dev(b_q), to_dev(b_s), to_dev(off),
+    h_q, h_s = moe.fp8_grouped_gemm_blockscaled(to_dev(a_q), to_dev(a_s), _packed(b_q), to_dev(b_s), to_dev(off),
                                                 moe.MOE_EPI_SWIGLU_QUANT, m_max=int(off[-1]))
     gu = gemm.grouped_gemm_blockscaled(a_q, a_s, None, b_q, b_s, off)
     from oracle.ffn import silu
