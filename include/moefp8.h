@@ -135,10 +135,10 @@ MOE_API int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, fl
  * MFMA-fragment order every GEMM of this library reads (offline, like the
  * 128x128 quantisation; not on the timed path).  Block (g, n16, kb) of 2048
  * bytes holds rows 16*n16..+15 and columns 128*kb..+127 of matrix g, blocks
- * ordered by (g, n16, kb), and inside a block byte h*1024 + r*64 + q*16 + b is
+ * ordered by (g, n16, kb), and inside a block byte h*1024 + (16*q + r)*16 + b is
  * B[16*n16 + r][128*kb + 64*h + 16*q + b].  One wave-wide 16-byte load then
- * reads 1 KB of consecutive bytes, exactly the B operands of a 16x16x128 MFMA,
- * and a 16-row slice's whole K range is one contiguous stream.  Scales are not
+ * reads 1 KB of consecutive bytes in lane order, exactly the B operands of a
+ * 16x16x128 MFMA, and a 16-row slice's whole K range is one contiguous stream.  Scales are not
  * reordered.  N % 16 == 0, K % 128 == 0; src and dst must not overlap.      */
 MOE_API int moe_pack_weights(const uint8_t* src, int G, int N, int K, uint8_t* dst, void* stream);
 

@@ -17,6 +17,7 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-ffp-contract=off",                     # no silent a*b+c fusion: rounding is written out explicitly
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",    # MFMA results in VGPRs: the fp32 scale promotion reads them directly
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) 
 #pragma unroll
     for (int nj = 0; nj < NT; ++nj) {
       const int blk = (nj >> 1) * 8 + wave * 2 + (nj & 1);
-      const uint8_t* fb = st + TL::kA + blk * 2048 + r16 * 64 + q * 16;
+      const uint8_t* fb = st + TL::kA + blk * 2048 + lane * 16;
       const u32x4 lo = *reinterpret_cast<const u32x4*>(fb);
       const u32x4 hi = *reinterpret_cast<const u32x4*>(fb + 1024);
       bf[nj] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   for (int f = 0; f < NF; ++f) {
     const int nb = f / NTW, j = f % NTW;
     const int n16 = wave_live ? (nb * half + ncol0) / 16 + j : 0;
-    b_ptr[f] = bq + (long)n16 * nkb * 2048 + r16 * 64 + q * 16;   // MFMA-fragment order: 1 KB per wave load
+    b_ptr[f] = bq + (long)n16 * nkb * 2048 + lane * 16;   // MFMA-fragment order: 1 KB per wave load
   }
   const float* sb_ptr[NB];
 #pragma unroll
@@ -560,6 +560,336 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// MFMA tile kernel for groups of many rows (prefill, dense layers).
+// Workgroup: 4 waves as 2 (rows) x 2 (columns); tile 32*MT rows x 256 B rows
+// (plain: 256 output columns; SwiGLU: 128 gate + 128 up rows = one 128-column
+// h tile).  Wave tile: 16*MT rows x 128 B rows (MT x 8 MFMA tiles).
+// Staging: A and B tiles of a K block go global -> LDS directly
+// (global_load_lds_dwordx4: each wave load writes 1 KB of LDS) in fragment
+// order, so every MFMA operand read is one 1 KB-contiguous ds_read_b128 at an
+// immediate offset; 3 LDS stages, one barrier per K block.  Per K block each
+// wave issues the same number of loads (kLoads), so "my loads for block kb are
+// done" is a constant vmcnt.
+constexpr int kStages = 3;
+
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+// Workgroup barrier without a memory fence: only the compiler is kept from
+// moving memory operations across it.  LDS-DMA data is covered by the explicit
+// vmcnt waits before it; __syncthreads() would also wait for every outstanding
+// load (vmcnt(0)) and empty the prefetch pipeline.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
+// expcnt and lgkmcnt left at their "no wait" maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int WM, int WN, int MT, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs args) {
+  constexpr int NW = WM * WN;                   // waves
+  constexpr int NTW = 16 / WN;                  // 16-column tiles per wave (the workgroup covers 256 B rows)
+  constexpr int BM = 16 * MT * WM;
+  constexpr bool kExact = EPI == kEpiSwiglu;
+  constexpr int A_BYTES = BM * 128, B_BYTES = 256 * 128, SA_BYTES = (BM / 32) * 256;
+  constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+  constexpr int A_LOADS = BM / 8 / NW;          // wave loads of A per wave per K block (2 per 16-row block)
+  constexpr int B_LOADS = 32 / NW;              // 16 blocks x 2 halves
+  constexpr int kLoads = A_LOADS + B_LOADS + 1; // + one scale load
+  static_assert(A_LOADS * NW == BM / 8 && B_LOADS * NW == 32, "loads must split evenly over the waves");
+  static_assert(BM / 32 <= NW && BM % 32 == 0, "one scale load per wave at most");
+  static_assert(!kExact || NTW % 2 == 0, "SwiGLU waves hold gate and up tiles in pairs");
+  // one array per pipeline stage: the compiler can then tell the stages apart and does
+  // not wait for every LDS-DMA load before each LDS read
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGE];
+  __shared__ int scan_tmp[256];
+  __shared__ int pre[1024];
+  __shared__ int pick[1];
+  __shared__ float red[WN][BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loads below
+  const int wm = wave % WM, wn = wave / WM;
+  int si, g, m0, m_end;
+  if (!find_tile(args, BM, scan_tmp, pre, pick, si, g, m0, m_end)) return;
+  const GemmSeg& s0 = args.seg[0];
+  const GemmSeg& s1 = args.seg[1];
+  const int K = si ? s1.K : s0.K, nkb = K >> 7;
+  const int Nfull = si ? s1.N : s0.N;
+  const int half = Nfull / (kExact ? 2 : 1);
+  const int nt = blockIdx.y;
+  if (nt * (kExact ? 128 : 256) >= half) return;
+  const uint8_t* const a_q = si ? s1.a_q : s0.a_q;
+  const float* const a_s = si ? s1.a_s : s0.a_s;
+  const int32_t* const gat = si ? s1.a_gather : s0.a_gather;
+  const uint8_t* const bq = (si ? s1.b_q : s0.b_q) + (long long)g * (si ? s1.b_stride : s0.b_stride);
+  const float* const bs = (si ? s1.b_s : s0.b_s) + (long long)g * (si ? s1.bs_stride : s0.bs_stride);
+
+  // ---- per-lane global sources of this wave's loads (advanced by kb each K block) ----
+  // A: wave load i covers 16-row block ab = (wave * A_LOADS + i) / 2, half h = i % 2;
+  //    lane (r16, q) loads row 16 ab + r16, bytes 64 h + 16 q: LDS slot = lane (fragment order).
+  const uint8_t* a_src[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int li = wave * A_LOADS + i;
+    const int ab = li >> 1, h = li & 1;
+    int m = m0 + ab * 16 + r16;
+    m = m < m_end ? m : m0;
+    const long src = gat ? (long)gat[m] : (long)m;
+    a_src[i] = a_q + src * K + 64 * h + 16 * q;
+  }
+  // B: wave load i covers local block bb = (wave * B_LOADS + i) / 2, half h = i % 2.
+  const uint8_t* b_src[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int li = wave * B_LOADS + i;
+    const int bb = li >> 1, h = li & 1;
+    const int n16 = kExact ? ((bb >> 3) * half + nt * 128) / 16 + (bb & 7) : (nt * 256) / 16 + bb;
+    const int n16c = n16 * 16 < Nfull ? n16 : 0;  // a partial last tile reads block 0 (discarded)
+    b_src[i] = bq + (long)n16c * nkb * 2048 + h * 1024 + lane * 16;
+  }
+  // scales of A rows: wave w loads the 32-row group min(w, BM/32 - 1) (lanes 32..63 repeat
+  // lanes 0..31) into 256 B of LDS; surplus waves rewrite the last group with the same
+  // values, which keeps every wave's load count equal
+  const int sgrp = wave < BM / 32 ? wave : BM / 32 - 1;
+  const float* sa_src;
+  {
+    int m = m0 + sgrp * 32 + (lane & 31);
+    m = m < m_end ? m : m0;
+    sa_src = a_s + (gat ? (long)gat[m] : (long)m) * nkb;
+  }
+  // scales of this wave's B blocks (wave-uniform): plain: one 128-column block; SwiGLU: gate and up
+  const float* sb_src0 = bs + (long)(kExact ? nt : (nt * 256 + wn * NTW * 16) / 128) * nkb;
+  const float* sb_src1 = bs + (long)(kExact ? (half + nt * 128) / 128 : 0) * nkb;
+
+#define MFMA_ISSUE(kb_, dst_)                                                                         \
+  {                                                                                                   \
+    uint8_t* st_ = (dst_);                                                                            \
+    _Pragma("unroll") for (int i = 0; i < A_LOADS; ++i)                                              \
+        lds_dma16(a_src[i] + (kb_) * 128, st_ + (wave * A_LOADS + i) * 1024);                         \
+    _Pragma("unroll") for (int i = 0; i < B_LOADS; ++i)                                              \
+        lds_dma16(b_src[i] + (long)(kb_) * 2048, st_ + A_BYTES + (wave * B_LOADS + i) * 1024);        \
+    lds_dma4(sa_src + (kb_), st_ + A_BYTES + B_BYTES + sgrp * 256);                                   \
+  }
+
+  v4f acc[MT][NTW];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int f = 0; f < NTW; ++f) acc[mi][f] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int lane_off = lane * 16;
+
+  // MFMAs and scale promotion of one K block from the LDS stage at st (+ this lane's offset)
+  auto compute = [&](const uint8_t* st, const float sb0, const float sb1) {
+    // B fragments of this wave: plain: local blocks NTW wn .. +NTW-1; SwiGLU: gate (NTW/2) wn .. and the
+    // same up blocks (+8)
+    v8i bf[NTW];
+#pragma unroll
+    for (int f = 0; f < NTW; ++f) {
+      constexpr int H = NTW / 2;
+      const int bb = kExact ? ((f / H) * 8 + wn * H + (f % H)) : (wn * NTW + f);
+      const v4i lo = *reinterpret_cast<const v4i*>(st + A_BYTES + bb * 2048);
+      const v4i hi = *reinterpret_cast<const v4i*>(st + A_BYTES + bb * 2048 + 1024);
+      bf[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      const int ab = wm * MT + mi;
+      const v4i lo = *reinterpret_cast<const v4i*>(st + ab * 2048);
+      const v4i hi = *reinterpret_cast<const v4i*>(st + ab * 2048 + 1024);
+      const v8i af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const int r0 = ab * 16;                   // the lane's rows are r0 + 4q .. +3
+      const float4 sa4 = *reinterpret_cast<const float4*>(st - lane_off + A_BYTES + B_BYTES + (r0 >> 5) * 256 +
+                                                          (r0 & 31) * 4 + q * 16);
+      const float c0[4] = {sa4.x * sb0, sa4.y * sb0, sa4.z * sb0, sa4.w * sb0};
+      const float c1[4] = {sa4.x * sb1, sa4.y * sb1, sa4.z * sb1, sa4.w * sb1};
+      v8bf ab8[4];
+      if constexpr (kExact) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ab8[j] = e4m3x8_to_bf16((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1]);
+      }
+#pragma unroll
+      for (int f0 = 0; f0 < NTW; f0 += 4) {       // promote in groups of 4 tiles: fewer live partials
+        v4f part[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int f = f0 + u;
+          if constexpr (kExact) {
+            v4f t = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  ab8[j], e4m3x8_to_bf16((uint32_t)bf[f][2 * j], (uint32_t)bf[f][2 * j + 1]), t, 0, 0, 0);
+            part[u] = t;
+          } else {
+            part[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[f], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                       0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[mi][f0 + u][i] = fmaf(part[u][i], (kExact && f0 + u >= NTW / 2) ? c1[i] : c0[i], acc[mi][f0 + u][i]);
+      }
+    }
+  };
+
+  // One K block: wait for this wave's loads of block kb (the loads of kb + 1 may stay in
+  // flight), barrier (everyone's block kb has landed and everyone is done with block kb - 1,
+  // whose stage the loads of kb + 2 now overwrite), issue kb + 2, compute kb.  The stage
+  // arrays are named statically (K loop unrolled by the 3 stages) so the compiler can tell
+  // them apart and keeps the other stages' loads in flight.
+#define MFMA_STEP(kb_, cur_, nxt_)                                                                    \
+  {                                                                                                   \
+    const int kbs = (kb_);                                                                            \
+    const float sb0 = sb_src0[kbs];                                                                   \
+    const float sb1 = kExact ? sb_src1[kbs] : sb0;                                                    \
+    if (kbs + 1 < nkb) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();                                    \
+    block_barrier();                                                                                  \
+    if (kbs + 2 < nkb) MFMA_ISSUE(kbs + 2, nxt_);                                                     \
+    compute((cur_) + lane_off, sb0, sb1);                                                             \
+  }
+
+  MFMA_ISSUE(0, smem0);
+  if (nkb > 1) MFMA_ISSUE(1, smem1);
+  for (int kb0 = 0; kb0 < nkb; kb0 += 3) {
+    MFMA_STEP(kb0, smem0, smem2);
+    if (kb0 + 1 < nkb) MFMA_STEP(kb0 + 1, smem1, smem0);
+    if (kb0 + 2 < nkb) MFMA_STEP(kb0 + 2, smem2, smem1);
+  }
+#undef MFMA_STEP
+#undef MFMA_ISSUE
+
+  void* const out = si ? s1.out : s0.out;
+  float* const out_s = si ? s1.out_s : s0.out_s;
+  const int ld_out = si ? s1.ld_out : s0.ld_out;
+  const int32_t* const dst_row = si ? s1.dst_row : s0.dst_row;
+  const float* const row_w = si ? s1.row_w : s0.row_w;
+  // lane holds rows wm*16*MT + 16 mi + 4q + i of the tile; plain: columns nt*256 + wn*16*NTW + 16 f + r16;
+  // SwiGLU: h columns nt*128 + wn*8*NTW + 16 j + r16 (gate f = j, up f = NTW/2 + j)
+  if constexpr (EPI == kEpiSwiglu) {
+    constexpr int H = NTW / 2;
+    float h[MT][H][4];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int j = 0; j < H; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][H + j][i]);
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < H; ++j) mx = fmaxf(mx, fabsf(h[mi][j][i]));
+        mx = group_max<16>(mx);
+        if (r16 == 0) red[wn][wm * 16 * MT + mi * 16 + 4 * q + i] = mx;
+      }
+    __syncthreads();                                // also: every wave is past its last LDS stage read
+    uint8_t* stage = smem0;                         // BM x 128 codes
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 16 * MT + mi * 16 + 4 * q + i;
+        float amax = red[0][r];
+#pragma unroll
+        for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[w2][r]);
+        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+#pragma unroll
+        for (int j = 0; j < H; ++j)
+          stage[r * 128 + wn * 16 * H + 16 * j + r16] = (uint8_t)e4m3_encode(h[mi][j][i] / sc);
+        if (wn == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + nt] = sc;
+      }
+    __syncthreads();
+    for (int ci = tid; ci < BM * 8; ci += 64 * NW) {
+      const int r = ci >> 3, c = ci & 7;
+      if (m0 + r < m_end)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(out) + (long)(m0 + r) * ld_out + nt * 128 + c * 16) =
+            *reinterpret_cast<const u32x4*>(stage + r * 128 + c * 16);
+    }
+  } else {
+    const int N = si ? s1.N : s0.N;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 16 * MT + mi * 16 + 4 * q + i;
+        if (m >= m_end) continue;
+        long dst = m;
+        float wgt = 1.0f;
+        if constexpr (EPI == kEpiScatter) {
+          dst = dst_row ? (long)dst_row[m] : (long)m;
+          wgt = row_w ? row_w[m] : 1.0f;
+        }
+#pragma unroll
+        for (int f = 0; f < NTW; ++f) {
+          const int n = nt * 256 + wn * 16 * NTW + 16 * f + r16;
+          if (n >= N) continue;
+          const float val = acc[mi][f][i];
+          if constexpr (EPI == kEpiF32) {
+            reinterpret_cast<float*>(out)[dst * ld_out + n] = val;
+          } else if constexpr (EPI == kEpiBf16) {
+            reinterpret_cast<uint16_t*>(out)[dst * ld_out + n] = f32_to_bf16_rne(val);
+          } else {
+            atomicAdd(reinterpret_cast<float*>(out) + dst * ld_out + n, wgt * val);
+          }
+        }
+      }
+  }
+}
+
+template <int WM, int WN, int MT, int EPI>
+static void launch_mfma_cfg(const GemmArgs& args, dim3 grid, hipStream_t st) {
+  mfma_gemm_kernel<WM, WN, MT, EPI><<<grid, 64 * WM * WN, 0, st>>>(args);
+}
+
+// bm = rows per tile: 32, 64 or 128.  The gate/up GEMM (exact bf16 path, VALU-heavier)
+// runs 8 waves with 64x64 wave tiles (two waves per SIMD co-issue VALU and MFMA);
+// the FP8 GEMMs run 4 waves with 64x128 wave tiles (half the LDS reads per MFMA).
+template <int MT>
+static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
+  const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
+  if (mt == 0) return hipSuccess;
+  const bool swiglu = epi == kEpiSwiglu;
+  int ny = 0;
+  for (int s = 0; s < 2; ++s) {
+    const GemmSeg& S = args.seg[s];
+    if (S.m_tiles > 0) {
+      const int n = swiglu ? (S.N / 2 + 127) / 128 : (S.N + 255) / 256;
+      ny = ny > n ? ny : n;
+    }
+  }
+  if (ny == 0) return hipSuccess;
+  const dim3 grid(mt, ny);
+  switch (epi) {
+    case kEpiSwiglu:
+      if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiSwiglu>(args, grid, st);
+      else launch_mfma_cfg<2, 2, MT, kEpiSwiglu>(args, grid, st);
+      break;
+    case kEpiF32: launch_mfma_cfg<2, 2, MT, kEpiF32>(args, grid, st); break;
+    case kEpiBf16: launch_mfma_cfg<2, 2, MT, kEpiBf16>(args, grid, st); break;
+    default: launch_mfma_cfg<2, 2, MT, kEpiScatter>(args, grid, st); break;
+  }
+  return hipGetLastError();
+}
+
 template <int BM>
 static hipError_t launch_bm(const GemmArgs& args, int epi, hipStream_t st) {
   const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
@@ -584,9 +914,9 @@ static hipError_t launch_bm(const GemmArgs& args, int epi, hipStream_t st) {
 hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st) {
   switch (bm) {
     case 16: return launch_stream(args, epi, st);
-    case 32: return launch_bm<32>(args, epi, st);
-    case 64: return launch_bm<64>(args, epi, st);
-    default: return launch_bm<128>(args, epi, st);
+    case 32: return launch_mfma<1>(args, epi, st);
+    case 64: return launch_mfma<2>(args, epi, st);
+    default: return launch_mfma<4>(args, epi, st);
   }
 }
 

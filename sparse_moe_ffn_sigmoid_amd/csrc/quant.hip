@@ -100,9 +100,10 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
 
 // Row-major e4m3 [G][N][K] -> MFMA-fragment order.  Block (g, n16, kb) holds
 // rows 16 n16 .. +15, columns 128 kb .. +127 in 2 KB: byte
-// (h * 1024 + r * 64 + q * 16 + b) = B[16 n16 + r][128 kb + 64 h + 16 q + b], so
-// the lane (r, q) of a 16x16x128 MFMA fragment finds its two 16-byte pieces at
-// h = 0 and h = 1, and one wave-wide load covers 1 KB of consecutive bytes.
+// (h * 1024 + (16 q + r) * 16 + b) = B[16 n16 + r][128 kb + 64 h + 16 q + b], so
+// lane l = r + 16 q of a 16x16x128 MFMA fragment finds its two 16-byte pieces at
+// h * 1024 + 16 l: one wave-wide load covers 1 KB of consecutive bytes in lane
+// order (bank-conflict free from LDS).
 __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ src, long nchunks, int N, int K,
                                                    uint4* __restrict__ dst) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;   // destination 16-byte chunk
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ src
   const int nkb = K >> 7;
   const long blk = i >> 7;                                // 2 KB block index (g, n16, kb)
   const int w = (int)(i & 127);
-  const int h = w >> 6, r = (w >> 2) & 15, q = w & 3;
+  const int h = w >> 6, r = w & 15, q = (w >> 4) & 3;
   const int kb = (int)(blk % nkb);
   const long gn16 = blk / nkb;                            // g * (N/16) + n16
   const long row = gn16 * 16 + r;                         // g * N + n

@@ -197,8 +197,8 @@ def test_pack_weights_layout():
     G, N, K = 3, 48, 384
     src = r.integers(0, 256, (G, N, K), dtype=np.uint8)
     got = moe.moe_pack_weights(to_dev(src)).cpu().numpy().reshape(-1)
-    # block (g, n16, kb) of 2048 bytes; byte h*1024 + r*64 + q*16 + b = B[16 n16 + r][128 kb + 64 h + 16 q + b]
-    want = src.reshape(G, N // 16, 16, K // 128, 2, 4, 16).transpose(0, 1, 3, 4, 2, 5, 6).reshape(-1)
+    # block (g, n16, kb) of 2048 bytes; byte h*1024 + (16 q + r)*16 + b = B[16 n16 + r][128 kb + 64 h + 16 q + b]
+    want = src.reshape(G, N // 16, 16, K // 128, 2, 4, 16).transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)
     assert np.array_equal(got, want)
 
 
