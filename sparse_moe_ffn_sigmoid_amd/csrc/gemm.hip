@@ -18,44 +18,32 @@
 // four 16x16x32 bf16 MFMAs per K block instead ("exact" path).  The down GEMM,
 // whose output is not requantised, keeps the native FP8 MFMA.
 //
-// Workgroup: 4 waves, BM rows x (128 * NB) B rows.  Every wave covers all BM
-// rows and 32 of each 128-row B block, so with NB = 2 (the gate/up GEMM, B rows
-// [gate block; up block]) a lane holds gate and up values of the same (row,
-// column) and SwiGLU is lane-local.  A and B tiles of one K block are staged
-// in LDS (16-byte chunks, XOR-swizzled by row so a 16-row fragment read is
-// bank-conflict free), double-buffered: the next block's global loads are in
-// flight while the current one feeds the MFMAs.
+// B is stored in MFMA-fragment order (moe_pack_weights): for 16 B rows and one
+// K block, 2 KB in which lane l of a wave finds its two 16-byte pieces at
+// 16 l and 1024 + 16 l, so every fragment load is one 1 KB-contiguous wave
+// access (coalesced from HBM, bank-conflict free in LDS).
 //
-// Grouped rows: a static segment (the shared expert, or a plain GEMM) takes the
-// first m tiles of the grid; a dynamic segment (routed experts) takes the rest,
-// and each workgroup finds its (group, tile) from the device-side offsets with
-// an in-LDS prefix sum over the groups' tile counts.  Tiles past the real
-// count exit at once, so no device-to-host copy of the counts is needed.
+// Two kernels:
+//  * stream_gemm_kernel (groups of <= 16 rows, decode): B bypasses LDS and
+//    streams from HBM into registers; the weight bytes are the whole cost.
+//  * mfma_gemm_kernel (larger groups, prefill and dense layers): A and B tiles
+//    go global -> LDS by LDS-DMA through a 3-stage pipeline, one barrier per
+//    K block.
+//
+// Grouped rows: a static segment (the shared expert, or a plain GEMM) and a
+// dynamic segment (routed experts, rows given by device-side offsets) share
+// one launch; each workgroup finds its tile with an in-LDS prefix sum over the
+// groups' tile counts, and workgroups past the real tile count exit at once,
+// so no device-to-host copy of the counts is needed.
 #include "common.h"
 #include "launch.h"
 
 namespace moefp8 {
 
-__device__ __forceinline__ int swz(int r, int c) { return (r << 7) + ((c ^ (r & 7)) << 4); }
-
-// Maps blockIdx.x to (segment, group, first row, end row) for tiles of bm
-// rows.  Static segment tiles come first; for the dynamic segment the
-// workgroup scans the groups' tile counts (offsets read on the device) in LDS.
-// Returns false (uniformly) for workgroups past the real tile count.
-__device__ bool find_tile(const GemmArgs& args, int bm, int* scan_tmp, int* pre, int* pick, int& si, int& g, int& m0,
-                          int& m_end) {
+// Inclusive prefix over the dynamic segment's per-group tile counts
+// ceil(rows_g / bm) into pre[0..G-1] (G <= 1024, 256 threads); returns the total.
+__device__ int group_tile_prefix(const GemmSeg& sd, int bm, int* scan_tmp, int* pre) {
   const int tid = threadIdx.x;
-  int v = blockIdx.x;
-  if (v < args.seg[0].m_tiles) {
-    si = 0;
-    g = 0;
-    m0 = v * bm;
-    m_end = args.seg[0].m_rows;
-    return true;
-  }
-  v -= args.seg[0].m_tiles;
-  const GemmSeg& sd = args.seg[1];
-  if (v >= sd.m_tiles) return false;
   const int G = sd.G;
   const int per = (G + 255) >> 8;               // groups per thread (G <= 1024)
   int cnt[4];
@@ -83,8 +71,13 @@ __device__ bool find_tile(const GemmArgs& args, int bm, int* scan_tmp, int* pre,
     if (i < per && gi < G) pre[gi] = run;       // inclusive prefix
   }
   __syncthreads();
-  if (tid == 0) {
-    int lo = 0, hi = G;                           // first group with pre[g] > v
+  return __builtin_amdgcn_readfirstlane(scan_tmp[255]);
+}
+
+// First group g with pre[g] > v (pre inclusive, non-decreasing); thread 0 searches, all read.
+__device__ int find_group(const int* pre, int G, int v, int* pick) {
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = G;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (pre[mid] > v) hi = mid; else lo = mid + 1;
@@ -92,262 +85,96 @@ __device__ bool find_tile(const GemmArgs& args, int bm, int* scan_tmp, int* pre,
     pick[0] = lo;
   }
   __syncthreads();
-  g = pick[0];
-  if (g >= G) return false;
+  return __builtin_amdgcn_readfirstlane(pick[0]);
+}
+
+// Maps blockIdx.x to (segment, group, first row, end row) for tiles of bm
+// rows (one workgroup per m tile; blockIdx.y is the n tile).  Static segment
+// tiles come first.  Returns false (uniformly) for workgroups past the real
+// tile count.  The tile coordinates are workgroup-uniform: readfirstlane lets
+// the compiler keep them (and every address derived from them) in scalar
+// registers.
+__device__ bool find_tile(const GemmArgs& args, int bm, int* scan_tmp, int* pre, int* pick, int& si, int& g, int& m0,
+                          int& m_end) {
+  int v = blockIdx.x;
+  if (v < args.seg[0].m_tiles) {
+    si = 0;
+    g = 0;
+    m0 = v * bm;
+    m_end = args.seg[0].m_rows;
+    return true;
+  }
+  v -= args.seg[0].m_tiles;
+  const GemmSeg& sd = args.seg[1];
+  if (v >= sd.m_tiles) return false;
+  const int total = group_tile_prefix(sd, bm, scan_tmp, pre);
+  if (v >= total) return false;
+  g = find_group(pre, sd.G, v, pick);
   si = 1;
   const int tiles_g = (sd.offsets[g + 1] - sd.offsets[g] + bm - 1) / bm;
-  m0 = sd.offsets[g] + (v - (pre[g] - tiles_g)) * bm;
-  m_end = sd.offsets[g + 1];
+  m0 = __builtin_amdgcn_readfirstlane(sd.offsets[g] + (v - (pre[g] - tiles_g)) * bm);
+  m_end = __builtin_amdgcn_readfirstlane(sd.offsets[g + 1]);
   return true;
 }
 
-template <int BM, int NB>
-struct Tile {
-  static constexpr int kA = BM * 128;            // A codes of one K block
-  static constexpr int kB = NB * 128 * 128;      // B codes of one K block
-  static constexpr int kSA = BM * 4;             // a_s of the BM rows
-  static constexpr int kSB = 16;                 // b_s of the NB blocks
-  static constexpr int kStage = kA + kB + kSA + kSB;
-};
+// Work order of the MFMA tile kernel.  A work item is one (m tile, n tile).
+// Items are numbered segment 0 first, then segment 1 group by group; inside a
+// group (or the static segment) the m tiles are taken in panels of up to
+// kPanel, and a panel's items run n-major with its m tiles innermost: the
+// items of one n tile, which read the same B tile, are adjacent, and a panel's
+// A rows are reused by every n tile of the panel.  The items are then cut into
+// 8 contiguous chunks of equal count, chunk x for XCD x: workgroups are
+// dispatched to the 8 XCDs round-robin by workgroup id, so workgroup b runs
+// item (b % 8) * chunk + b / 8, and each XCD's L2 sees a contiguous run of
+// items (one expert's tiles land on one XCD and share its L2).
+constexpr int kPanel = 4;
 
-template <int BM, int NB, int EPI>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs args) {
-  using TL = Tile<BM, NB>;
-  constexpr int MT = BM / 16;                 // 16-row tiles per wave
-  constexpr int NT = 2 * NB;                  // 16-col tiles per wave
-  constexpr int BN = 128 * NB;
-  constexpr int A_CH = BM * 8;                // 16-byte chunks per K block
-  constexpr int A_PER = (A_CH + 255) / 256;
-  constexpr int B_PER = BN * 8 / 256;
-  constexpr bool kExact = EPI == kEpiSwiglu;   // requantised output: exact-accumulating bf16 MFMA
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::kStage];
-  __shared__ int scan_tmp[256];
-  __shared__ int pre[1024];
-  __shared__ int pick[1];
-  __shared__ float red[4][BM];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
-  const int nt = blockIdx.y;
-  int si, g, m0, m_end;
-  if (!find_tile(args, BM, scan_tmp, pre, pick, si, g, m0, m_end)) return;
-  // this tile's segment, field by field (kept in scalar registers)
-  const GemmSeg& s0 = args.seg[0];
-  const GemmSeg& s1 = args.seg[1];
-  const int K = si ? s1.K : s0.K, nkb = K >> 7;
-  const uint8_t* const a_q = si ? s1.a_q : s0.a_q;
-  const float* const a_s = si ? s1.a_s : s0.a_s;
-  const int32_t* const gat = si ? s1.a_gather : s0.a_gather;
-  const int half = (si ? s1.N : s0.N) / NB;     // B rows per block (N for NB = 1, W for SwiGLU)
-  if (nt * 128 >= half) return;
-  const uint8_t* const bq = (si ? s1.b_q : s0.b_q) + (long long)g * (si ? s1.b_stride : s0.b_stride);
-  const float* const bs = (si ? s1.b_s : s0.b_s) + (long long)g * (si ? s1.bs_stride : s0.bs_stride);
-
-  // per-thread global sources of the 16-byte chunks it stages each K block
-  const uint8_t* a_src[A_PER];
-  int a_dst[A_PER];
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int ci = tid + 256 * i;
-    const int r = (ci >> 3) < BM ? (ci >> 3) : 0;
-    const int m = m0 + r < m_end ? m0 + r : m0;
-    const long src = gat ? (long)gat[m] : (long)m;
-    a_src[i] = a_q + src * K + ((ci & 7) << 4);
-    a_dst[i] = swz(r, ci & 7);
-  }
-  // B is in MFMA-fragment order: the tile's K block is NB x 8 contiguous 2 KB
-  // blocks (16 rows each); LDS keeps that order, so fragment reads are 1 KB
-  // contiguous per wave instruction (no bank conflicts, no swizzle needed).
-  const uint8_t* b_src[B_PER];
-  int b_dst[B_PER];
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int ci = tid + 256 * i;
-    const int blk = ci >> 7;                      // local 16-row block: nb * 8 + n16
-    const int n16 = ((blk >> 3) * half + nt * 128) / 16 + (blk & 7);
-    b_src[i] = bq + (long)n16 * nkb * 2048 + ((ci & 127) << 4);
-    b_dst[i] = TL::kA + (ci << 4);
-  }
-  // thread tid < BM stages a_s of row tid; threads BM .. BM+NB-1 stage b_s of block tid-BM
-  const float* s_src = nullptr;
-  int s_dst = 0;
-  if (tid < BM) {
-    const int m = m0 + tid < m_end ? m0 + tid : m0;
-    const long src = gat ? (long)gat[m] : (long)m;
-    s_src = a_s + src * nkb;
-    s_dst = TL::kA + TL::kB + tid * 4;
-  } else if (tid < BM + NB) {
-    s_src = bs + (long)((((tid - BM) * half) + nt * 128) >> 7) * nkb;
-    s_dst = TL::kA + TL::kB + TL::kSA + (tid - BM) * 4;
-  }
-
-  u32x4 ra[A_PER], rb[B_PER];
-  float rs = 0.0f;
-#define GEMM_GLOAD(kb_)                                                                      \
-  {                                                                                          \
-    const int ko_ = (kb_) << 7;                                                              \
-    _Pragma("unroll") for (int i = 0; i < A_PER; ++i) ra[i] =                               \
-        *reinterpret_cast<const u32x4*>(a_src[i] + ko_);                                     \
-    _Pragma("unroll") for (int i = 0; i < B_PER; ++i) rb[i] =                               \
-        *reinterpret_cast<const u32x4*>(b_src[i] + (long)(kb_) * 2048);                      \
-    if (s_src) rs = s_src[kb_];                                                              \
-  }
-#define GEMM_SSTORE(buf_)                                                                    \
-  {                                                                                          \
-    uint8_t* st_ = smem + (buf_) * TL::kStage;                                               \
-    _Pragma("unroll") for (int i = 0; i < A_PER; ++i) if ((tid + 256 * i) < A_CH)           \
-        *reinterpret_cast<u32x4*>(st_ + a_dst[i]) = ra[i];                                   \
-    _Pragma("unroll") for (int i = 0; i < B_PER; ++i)                                       \
-        *reinterpret_cast<u32x4*>(st_ + b_dst[i]) = rb[i];                                   \
-    if (s_src) *reinterpret_cast<float*>(st_ + s_dst) = rs;                                  \
-  }
-
-  v4f acc[MT][NT];
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < NT; ++nj) acc[mi][nj] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  GEMM_GLOAD(0);
-  GEMM_SSTORE(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) GEMM_GLOAD(kb + 1);
-    const uint8_t* st = smem + cur * TL::kStage;
-    v8i af[MT], bf[NT];
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      const int r = mi * 16 + r16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + swz(r, q));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + swz(r, q + 4));
-      af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int nj = 0; nj < NT; ++nj) {
-      const int blk = (nj >> 1) * 8 + wave * 2 + (nj & 1);
-      const uint8_t* fb = st + TL::kA + blk * 2048 + lane * 16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(fb);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(fb + 1024);
-      bf[nj] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    const float* sa = reinterpret_cast<const float*>(st + TL::kA + TL::kB);
-    const float* sb = reinterpret_cast<const float*>(st + TL::kA + TL::kB + TL::kSA);
-    v4f part[MT][NT];
-    if constexpr (kExact) {
-      // lane bytes [8j, 8j+8) of its 32 feed bf16 MFMA j: the same K mapping on both operands
-      v8bf ab[MT][4], bb[NT][4];
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ab[mi][j] = e4m3x8_to_bf16((uint32_t)af[mi][2 * j], (uint32_t)af[mi][2 * j + 1]);
-#pragma unroll
-      for (int nj = 0; nj < NT; ++nj)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bb[nj][j] = e4m3x8_to_bf16((uint32_t)bf[nj][2 * j], (uint32_t)bf[nj][2 * j + 1]);
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NT; ++nj) {
-          v4f p = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[mi][j], bb[nj][j], p, 0, 0, 0);
-          part[mi][nj] = p;
-        }
-    } else {
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NT; ++nj)
-          part[mi][nj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mi], bf[nj], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                           0, 0, 0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      const float4 s4 = *reinterpret_cast<const float4*>(sa + mi * 16 + 4 * q);
-      const float sav[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float sbv = sb[nb];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float scl = sav[i] * sbv;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[mi][2 * nb + j][i] = fmaf(part[mi][2 * nb + j][i], scl, acc[mi][2 * nb + j][i]);
-        }
-      }
-    }
-    if (kb + 1 < nkb) GEMM_SSTORE(cur ^ 1);
-    __syncthreads();
-  }
-
-#undef GEMM_GLOAD
-#undef GEMM_SSTORE
-  // ---- epilogues: lane holds rows m0 + mi*16 + 4q + i, column wave*32 + j*16 + r16 of each B block ----
-  void* const out = si ? s1.out : s0.out;
-  float* const out_s = si ? s1.out_s : s0.out_s;
-  const int ld_out = si ? s1.ld_out : s0.ld_out;
-  const int32_t* const dst_row = si ? s1.dst_row : s0.dst_row;
-  const float* const row_w = si ? s1.row_w : s0.row_w;
-  if constexpr (EPI == kEpiSwiglu) {
-    float h[MT][2][4];
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][2 + j][i]);
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = fmaxf(fabsf(h[mi][0][i]), fabsf(h[mi][1][i]));
-        mx = group_max<16>(mx);
-        if (r16 == 0) red[wave][mi * 16 + 4 * q + i] = mx;
-      }
-    __syncthreads();
-    uint8_t* stage = smem;                        // BM x 128 codes, row-major
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mi * 16 + 4 * q + i;
-        const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) stage[r * 128 + wave * 32 + j * 16 + r16] = (uint8_t)e4m3_encode(h[mi][j][i] / sc);
-        if (wave == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + nt] = sc;
-      }
-    __syncthreads();
-    uint8_t* hq = reinterpret_cast<uint8_t*>(out);
-    for (int ci = tid; ci < BM * 8; ci += 256) {
-      const int r = ci >> 3, c = ci & 7;
-      if (m0 + r < m_end)
-        *reinterpret_cast<u32x4*>(hq + (long)(m0 + r) * ld_out + nt * 128 + c * 16) =
-            *reinterpret_cast<const u32x4*>(stage + r * 128 + c * 16);
-    }
+__device__ __forceinline__ void panel_map(int L, int c, int ny, int& mt, int& nt) {
+  const int full = c / kPanel;                  // full panels of kPanel m tiles
+  const int in_full = full * kPanel * ny;
+  if (L < in_full) {
+    const int p = L / (kPanel * ny), r = L - p * (kPanel * ny);
+    nt = r / kPanel;
+    mt = p * kPanel + (r - nt * kPanel);
   } else {
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + mi * 16 + 4 * q + i;
-        if (m >= m_end) continue;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = nt * 128 + wave * 32 + j * 16 + r16;
-          const float val = acc[mi][j][i];
-          if constexpr (EPI == kEpiF32) {
-            reinterpret_cast<float*>(out)[(long)m * ld_out + n] = val;
-          } else if constexpr (EPI == kEpiBf16) {
-            reinterpret_cast<uint16_t*>(out)[(long)m * ld_out + n] = f32_to_bf16_rne(val);
-          } else {
-            const long dst = dst_row ? (long)dst_row[m] : (long)m;
-            const float wgt = row_w ? row_w[m] : 1.0f;
-            atomicAdd(reinterpret_cast<float*>(out) + dst * ld_out + n, wgt * val);
-          }
-        }
-      }
+    const int rem = c - full * kPanel, r = L - in_full;
+    nt = r / rem;
+    mt = full * kPanel + (r - nt * rem);
   }
+}
+
+__device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int* scan_tmp, int* pre, int* pick,
+                          int& si, int& g, int& m0, int& m_end, int& nt) {
+  const GemmSeg& s0 = args.seg[0];
+  const GemmSeg& sd = args.seg[1];
+  const int w0 = s0.m_tiles * ny0;
+  const int c1 = sd.m_tiles > 0 ? group_tile_prefix(sd, bm, scan_tmp, pre) : 0;
+  const int total = w0 + c1 * ny1;
+  const int chunk = (total + 7) >> 3;
+  const int b = blockIdx.x, j = b >> 3;
+  if (j >= chunk) return false;
+  const int w = (b & 7) * chunk + j;
+  if (w >= total) return false;
+  int mt;
+  if (w < w0) {
+    panel_map(w, s0.m_tiles, ny0, mt, nt);
+    si = 0;
+    g = 0;
+    m0 = mt * bm;
+    m_end = s0.m_rows;
+  } else {
+    const int v = w - w0;
+    g = find_group(pre, sd.G, v / ny1, pick);
+    const int c = (sd.offsets[g + 1] - sd.offsets[g] + bm - 1) / bm;
+    panel_map(v - ny1 * (pre[g] - c), c, ny1, mt, nt);
+    si = 1;
+    m0 = sd.offsets[g] + mt * bm;
+    m_end = sd.offsets[g + 1];
+  }
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  m_end = __builtin_amdgcn_readfirstlane(m_end);
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -624,15 +451,15 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loads below
   const int wm = wave % WM, wn = wave / WM;
-  int si, g, m0, m_end;
-  if (!find_tile(args, BM, scan_tmp, pre, pick, si, g, m0, m_end)) return;
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& s1 = args.seg[1];
+  const int ny0 = kExact ? s0.N / 256 : (s0.N + 255) / 256;   // n tiles per segment
+  const int ny1 = kExact ? s1.N / 256 : (s1.N + 255) / 256;
+  int si, g, m0, m_end, nt;
+  if (!find_work(args, BM, ny0, ny1, scan_tmp, pre, pick, si, g, m0, m_end, nt)) return;
   const int K = si ? s1.K : s0.K, nkb = K >> 7;
   const int Nfull = si ? s1.N : s0.N;
   const int half = Nfull / (kExact ? 2 : 1);
-  const int nt = blockIdx.y;
-  if (nt * (kExact ? 128 : 256) >= half) return;
   const uint8_t* const a_q = si ? s1.a_q : s0.a_q;
   const float* const a_s = si ? s1.a_s : s0.a_s;
   const int32_t* const gat = si ? s1.a_gather : s0.a_gather;
@@ -662,19 +489,25 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
     const int n16c = n16 * 16 < Nfull ? n16 : 0;  // a partial last tile reads block 0 (discarded)
     b_src[i] = bq + (long)n16c * nkb * 2048 + h * 1024 + lane * 16;
   }
-  // scales of A rows: wave w loads the 32-row group min(w, BM/32 - 1) (lanes 32..63 repeat
-  // lanes 0..31) into 256 B of LDS; surplus waves rewrite the last group with the same
-  // values, which keeps every wave's load count equal
+  // Scales, one 4-byte LDS-DMA per wave and K block into a 256 B slot: wave w loads the A-row
+  // scales of the 32-row group min(w, BM/32 - 1) with lanes 0..31 (surplus waves rewrite the
+  // last group with the same values, which keeps every wave's load count equal); lanes 32 and
+  // 33 load the tile's two B-scale blocks (plain: columns nt*256 and nt*256 + 128; SwiGLU: the
+  // gate and the up block), so the B scales arrive with the stage, under the same vmcnt wait;
+  // lanes 34..63 repeat A rows.
   const int sgrp = wave < BM / 32 ? wave : BM / 32 - 1;
   const float* sa_src;
-  {
+  if (lane == 32 || lane == 33) {
+    int blk = kExact ? (lane == 32 ? nt : (half + nt * 128) / 128) : 2 * nt + (lane - 32);
+    blk = blk * 128 < Nfull ? blk : 2 * nt;       // a partial last tile: the missing block is never stored
+    sa_src = bs + (long)blk * nkb;
+  } else {
     int m = m0 + sgrp * 32 + (lane & 31);
     m = m < m_end ? m : m0;
     sa_src = a_s + (gat ? (long)gat[m] : (long)m) * nkb;
   }
-  // scales of this wave's B blocks (wave-uniform): plain: one 128-column block; SwiGLU: gate and up
-  const float* sb_src0 = bs + (long)(kExact ? nt : (nt * 256 + wn * NTW * 16) / 128) * nkb;
-  const float* sb_src1 = bs + (long)(kExact ? (half + nt * 128) / 128 : 0) * nkb;
+  // this wave's B-scale slot(s): plain: the 128-column block its columns fall in; SwiGLU: gate, up
+  const int sb_slot = kExact ? 0 : (wn * NTW * 16) / 128;
 
 #define MFMA_ISSUE(kb_, dst_)                                                                         \
   {                                                                                                   \
@@ -692,9 +525,25 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 #pragma unroll
     for (int f = 0; f < NTW; ++f) acc[mi][f] = v4f{0.f, 0.f, 0.f, 0.f};
   const int lane_off = lane * 16;
+  // A wave whose rows all lie past the group's end (the last tile of a group is often partial)
+  // only loads and synchronises; one uniform branch around the whole K block keeps the MFMA
+  // schedule inside it intact.
+  const bool wave_has_rows = m0 + wm * 16 * MT < m_end;
 
   // MFMAs and scale promotion of one K block from the LDS stage at st (+ this lane's offset)
-  auto compute = [&](const uint8_t* st, const float sb0, const float sb1) {
+  auto compute = [&](const uint8_t* st) {
+    auto load_a = [&](int mi) {
+      const int ab = wm * MT + mi;
+      const v4i lo = *reinterpret_cast<const v4i*>(st + ab * 2048);
+      const v4i hi = *reinterpret_cast<const v4i*>(st + ab * 2048 + 1024);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // LDS reads in the order the MFMAs need them: the first A fragment, then the B fragments;
+    // the next A fragment is read one row block ahead
+    v8i af_next = load_a(0);
+    const float* sbp = reinterpret_cast<const float*>(st - lane_off + A_BYTES + B_BYTES + 128);
+    const float sb0 = sbp[sb_slot];
+    const float sb1 = kExact ? sbp[1] : sb0;
     // B fragments of this wave: plain: local blocks NTW wn .. +NTW-1; SwiGLU: gate (NTW/2) wn .. and the
     // same up blocks (+8)
     v8i bf[NTW];
@@ -709,9 +558,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       const int ab = wm * MT + mi;
-      const v4i lo = *reinterpret_cast<const v4i*>(st + ab * 2048);
-      const v4i hi = *reinterpret_cast<const v4i*>(st + ab * 2048 + 1024);
-      const v8i af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const v8i af = af_next;
+      if (mi + 1 < MT) af_next = load_a(mi + 1);
       const int r0 = ab * 16;                   // the lane's rows are r0 + 4q .. +3
       const float4 sa4 = *reinterpret_cast<const float4*>(st - lane_off + A_BYTES + B_BYTES + (r0 >> 5) * 256 +
                                                           (r0 & 31) * 4 + q * 16);
@@ -753,25 +601,39 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   // flight), barrier (everyone's block kb has landed and everyone is done with block kb - 1,
   // whose stage the loads of kb + 2 now overwrite), issue kb + 2, compute kb.  The stage
   // arrays are named statically (K loop unrolled by the 3 stages) so the compiler can tell
-  // them apart and keeps the other stages' loads in flight.
+  // them apart and keeps the other stages' loads in flight.  The main loop has no branches
+  // inside: with control flow in the loop body the compiler's wait insertion loses track of
+  // which stage a pending LDS-DMA load writes and waits for all of them before LDS reads.
+  // The last one to four blocks run in a peeled tail with the bounds checks.
 #define MFMA_STEP(kb_, cur_, nxt_)                                                                    \
   {                                                                                                   \
+    wait_vmcnt<kLoads>();                                                                             \
+    block_barrier();                                                                                  \
+    MFMA_ISSUE((kb_) + 2, nxt_);                                                                      \
+    if (wave_has_rows) compute((cur_) + lane_off);                                                    \
+  }
+#define MFMA_STEP_TAIL(kb_, cur_, nxt_)                                                               \
+  {                                                                                                   \
     const int kbs = (kb_);                                                                            \
-    const float sb0 = sb_src0[kbs];                                                                   \
-    const float sb1 = kExact ? sb_src1[kbs] : sb0;                                                    \
     if (kbs + 1 < nkb) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();                                    \
     block_barrier();                                                                                  \
     if (kbs + 2 < nkb) MFMA_ISSUE(kbs + 2, nxt_);                                                     \
-    compute((cur_) + lane_off, sb0, sb1);                                                             \
+    if (wave_has_rows) compute((cur_) + lane_off);                                                    \
   }
 
   MFMA_ISSUE(0, smem0);
-  if (nkb > 1) MFMA_ISSUE(1, smem1);
-  for (int kb0 = 0; kb0 < nkb; kb0 += 3) {
+  MFMA_ISSUE(nkb > 1 ? 1 : 0, smem1);           // unconditional (no branch before the loop); for
+  int kb0 = 0;                                  // nkb == 1 a copy of block 0 that is never read
+  for (; kb0 + 4 < nkb; kb0 += 3) {             // every step here issues block kb + 2 < nkb
     MFMA_STEP(kb0, smem0, smem2);
-    if (kb0 + 1 < nkb) MFMA_STEP(kb0 + 1, smem1, smem0);
-    if (kb0 + 2 < nkb) MFMA_STEP(kb0 + 2, smem2, smem1);
+    MFMA_STEP(kb0 + 1, smem1, smem0);
+    MFMA_STEP(kb0 + 2, smem2, smem1);
   }
+  MFMA_STEP_TAIL(kb0, smem0, smem2);              // 1 to 4 blocks remain; kb0 is a multiple of 3
+  if (kb0 + 1 < nkb) MFMA_STEP_TAIL(kb0 + 1, smem1, smem0);
+  if (kb0 + 2 < nkb) MFMA_STEP_TAIL(kb0 + 2, smem2, smem1);
+  if (kb0 + 3 < nkb) MFMA_STEP_TAIL(kb0 + 3, smem0, smem2);
+#undef MFMA_STEP_TAIL
 #undef MFMA_STEP
 #undef MFMA_ISSUE
 
@@ -865,19 +727,14 @@ static void launch_mfma_cfg(const GemmArgs& args, dim3 grid, hipStream_t st) {
 // the FP8 GEMMs run 4 waves with 64x128 wave tiles (half the LDS reads per MFMA).
 template <int MT>
 static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
-  const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
-  if (mt == 0) return hipSuccess;
   const bool swiglu = epi == kEpiSwiglu;
-  int ny = 0;
+  long items = 0;                               // upper bound of the work items (m tiles reserved x n tiles)
   for (int s = 0; s < 2; ++s) {
     const GemmSeg& S = args.seg[s];
-    if (S.m_tiles > 0) {
-      const int n = swiglu ? (S.N / 2 + 127) / 128 : (S.N + 255) / 256;
-      ny = ny > n ? ny : n;
-    }
+    if (S.m_tiles > 0) items += (long)S.m_tiles * (swiglu ? S.N / 256 : (S.N + 255) / 256);
   }
-  if (ny == 0) return hipSuccess;
-  const dim3 grid(mt, ny);
+  if (items == 0) return hipSuccess;
+  const dim3 grid((unsigned)(8 * ((items + 7) / 8)));   // whole rounds over the 8 XCDs
   switch (epi) {
     case kEpiSwiglu:
       if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiSwiglu>(args, grid, st);
@@ -886,27 +743,6 @@ static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
     case kEpiF32: launch_mfma_cfg<2, 2, MT, kEpiF32>(args, grid, st); break;
     case kEpiBf16: launch_mfma_cfg<2, 2, MT, kEpiBf16>(args, grid, st); break;
     default: launch_mfma_cfg<2, 2, MT, kEpiScatter>(args, grid, st); break;
-  }
-  return hipGetLastError();
-}
-
-template <int BM>
-static hipError_t launch_bm(const GemmArgs& args, int epi, hipStream_t st) {
-  const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
-  if (mt == 0) return hipSuccess;
-  int nt = 0;
-  const int nb = epi == kEpiSwiglu ? 2 : 1;
-  for (int s = 0; s < 2; ++s) {
-    const GemmSeg& S = args.seg[s];
-    if (S.m_tiles > 0) nt = nt > S.N / nb / 128 ? nt : S.N / nb / 128;
-  }
-  if (nt == 0) return hipSuccess;
-  const dim3 grid(mt, nt);
-  switch (epi) {
-    case kEpiSwiglu: grouped_gemm_kernel<BM, 2, kEpiSwiglu><<<grid, 256, 0, st>>>(args); break;
-    case kEpiF32: grouped_gemm_kernel<BM, 1, kEpiF32><<<grid, 256, 0, st>>>(args); break;
-    case kEpiBf16: grouped_gemm_kernel<BM, 1, kEpiBf16><<<grid, 256, 0, st>>>(args); break;
-    default: grouped_gemm_kernel<BM, 1, kEpiScatter><<<grid, 256, 0, st>>>(args); break;
   }
   return hipGetLastError();
 }
