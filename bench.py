@@ -13,7 +13,17 @@ workload is the V3-shape decode step (T=64).
 Prints one JSON line.  ``roofline`` describes the dominant kernel (the gate/up
 grouped GEMM) from HIP events recorded on the launch stream between the
 library's stages; ``cpu_baseline`` times the CPU oracle on a bounded token
-sample of the same workload.
+sample of the same workload.  ``roofline.traffic`` is the HBM traffic per launch
+of that kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, stored in
+profiles/<workload>_gate_up_traffic.md together with a hash of the GEMM sources;
+it is reported only while the sources still match (else null).
+
+Helpers for the counter runs:
+  --calibrate-copy MIB     a plain copy of MIB MiB (the library's row gather with the identity
+                           permutation): the counters' scale factor.
+  --traffic-summary DIR    turns the four counter runs under DIR (fetch/, write/, copy_fetch/,
+                           copy_write/; commands in the written file) into
+                           profiles/<workload>_gate_up_traffic.md.
 """
 from __future__ import annotations
 
@@ -95,6 +105,124 @@ def build_layer(shape, dev):
     return moe.MoeWeights(**kw)
 
 
+COPY_MIB = 2048
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/launch.h")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "sparse_moe_ffn_sigmoid_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gate_up_kernel(shape) -> str:
+    """Name of the kernel the library runs for the gate/up GEMM of this shape (the library picks
+    the weight-streaming kernel when groups average at most 16 rows, else the MFMA tile kernel
+    with 64 rows per wave for groups above 64 rows)."""
+    rows = shape.tokens * shape.top_k / shape.n_experts if shape.n_experts else shape.tokens
+    if rows <= 16:
+        return "stream_gemm_kernel<2, 2, 4, 2>"
+    mt = 1 if rows <= 32 else 2 if rows <= 64 else 4
+    return f"mfma_gemm_kernel<2, {4 if mt >= 2 else 2}, {mt}, 2>"
+
+
+def traffic_file(shape) -> str:
+    return os.path.join(ROOT, "profiles", f"{shape.name}_gate_up_traffic.md")
+
+
+def stored_traffic(shape):
+    """HBM bytes per launch of the gate/up kernel from the stored counter summary, or None when
+    there is none or the GEMM sources changed since the counters were taken."""
+    try:
+        text = open(traffic_file(shape)).read()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes_per_launch: ",
+                                                                           "source_sha256: ")))
+    if kv.get("source_sha256") != gemm_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain copy of known size: moe_permute with one expert and k = 1 gathers rows by the
+    identity permutation, so its gather kernel (one 16-byte chunk per lane, consecutive lanes on
+    consecutive chunks) reads mib MiB of rows (+ 4 bytes of index per row) and writes mib MiB."""
+    import torch
+
+    import sparse_moe_ffn_sigmoid_amd as moe
+    rows = torch.ones((mib, 1 << 20), dtype=torch.uint8, device="cuda")
+    idx = torch.zeros((mib, 1), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out = moe.moe_permute(idx, 1, rows)[3]
+        del out
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": mib << 20, "dispatches": 3}))
+
+
+def _counter_means(d: str, counter: str, substr: str):
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {substr!r} under {d}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(d: str, shape) -> None:
+    kern = gate_up_kernel(shape)
+    f_k, n_f = _counter_means(os.path.join(d, "fetch"), "FETCH_SIZE", kern)
+    w_k, n_w = _counter_means(os.path.join(d, "write"), "WRITE_SIZE", kern)
+    f_c, _ = _counter_means(os.path.join(d, "copy_fetch"), "FETCH_SIZE", "perm_gather_kernel")
+    w_c, _ = _counter_means(os.path.join(d, "copy_write"), "WRITE_SIZE", "perm_gather_kernel")
+    n = COPY_MIB << 20
+    ff, fw = (n + 4 * COPY_MIB) / (f_c * 1024), n / (w_c * 1024)
+    traffic = f_k * 1024 * ff + w_k * 1024 * fw
+    bench = f"python3 $R/bench.py --workload {shape.name} --steps 3 --warmup 1 --no-cpu-baseline"
+    run = "timeout -s KILL 90 rocprofv3 --pmc {c} -f csv -d $R/gpurun_out/traffic/{o} -o {o} -- {cmd}"
+    lines = [
+        f"# HBM traffic of the gate/up GEMM kernel, {shape.name}",
+        "",
+        "Counter runs (one counter per run, R = repository root, from `cd /tmp && export TMPDIR=/tmp`):",
+        "",
+        "```",
+        run.format(c="FETCH_SIZE", o="fetch", cmd=bench),
+        run.format(c="WRITE_SIZE", o="write", cmd=bench),
+        run.format(c="FETCH_SIZE", o="copy_fetch", cmd=f"python3 $R/bench.py --calibrate-copy {COPY_MIB}"),
+        run.format(c="WRITE_SIZE", o="copy_write", cmd=f"python3 $R/bench.py --calibrate-copy {COPY_MIB}"),
+        f"python3 bench.py --workload {shape.name} --traffic-summary gpurun_out/traffic",
+        "```",
+        "",
+        f"Kernel: `{kern}` ({n_f} and {n_w} dispatches). Counters are KiB per dispatch.",
+        "The copy kernel is the library's row gather (moe_permute with one expert and k = 1: the",
+        "identity permutation of 1 MiB rows, one 16-byte chunk per lane), which reads and writes",
+        f"{COPY_MIB} MiB (+ 4 bytes of index per row); the factors scale each counter to bytes.",
+        "",
+        "```",
+        f"kernel_FETCH_SIZE_KiB: {f_k:.1f}",
+        f"kernel_WRITE_SIZE_KiB: {w_k:.1f}",
+        f"copy_FETCH_SIZE_KiB: {f_c:.1f}",
+        f"copy_WRITE_SIZE_KiB: {w_c:.1f}",
+        f"fetch_factor: {ff:.4f}",
+        f"write_factor: {fw:.4f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"source_sha256: {gemm_source_hash()}",
+        "```",
+        "",
+    ]
+    with open(traffic_file(shape), "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {traffic_file(shape)}: {traffic / 1e9:.3f} GB per launch")
+
+
 def algorithmic_bytes(shape, touched: int) -> dict:
     """Bytes the method must move (codes + scales of experts with load > 0 and the shared
     expert, router weights and bias, x in and the output, both bf16)."""
@@ -156,7 +284,16 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, metavar="MIB")
+    ap.add_argument("--traffic-summary", metavar="DIR")
     args = ap.parse_args()
+    if args.traffic_summary:
+        import synth
+        traffic_summary(args.traffic_summary, synth.SHAPES[args.workload])
+        return
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -238,8 +375,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": gate_up_flops / t_gu / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "grouped_gemm_kernel (gate/up, SwiGLU+requant epilogue)"
+    roof["traffic"] = stored_traffic(shape)
+    roof["kernel"] = gate_up_kernel(shape) + " (gate/up GEMM, SwiGLU + requantisation epilogue)"
     roof["avg_ms"] = stage["gate_up_gemm"]
     attainable = max(flops / (FP8_PEAK_TFLOPS * 1e12), nbytes["layer"] / (HBM_PEAK_GBS * 1e9))
 
