@@ -19,6 +19,15 @@ def loads(topk_idx: np.ndarray, n_experts: int) -> np.ndarray:
     return np.bincount(np.asarray(topk_idx).reshape(-1), minlength=n_experts)
 
 
+def update(bias: np.ndarray, topk_idx: np.ndarray, n_experts: int, gamma: float) -> np.ndarray:
+    """One balancing step of the routing bias after a batch: the target of every expert is the
+    mean load T*k/E, so an overloaded expert's bias drops by gamma, an underloaded one's rises by
+    gamma, and an expert exactly at the mean keeps its bias (fp32 add)."""
+    ld = loads(topk_idx, n_experts)
+    mean = np.asarray(topk_idx).size / n_experts
+    return adjust(bias, ld, np.full(n_experts, mean), gamma)
+
+
 def adjust(bias: np.ndarray, load: np.ndarray, target: np.ndarray, gamma: float) -> np.ndarray:
     step = np.sign(np.asarray(target, np.float64) - load).astype(np.float32)
     return (bias + np.float32(gamma) * step).astype(np.float32)

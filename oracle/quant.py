@@ -10,6 +10,13 @@ section bodies are missing from the page, so the oracle takes this reading:
 * per tile/block: amax = max |v| (exact), s = fp32(amax / 448) with a
   correctly rounded fp32 division, q_i = E4M3(fp32(v_i / s)) with a correctly
   rounded fp32 division; an all-zero tile gets s = 1 and codes 0x00.
+
+Power-of-two ("UE8M0") variant ([arch blog] "More Mantissa bits of fp8": a
+customised data format and scaling factor; the section body is missing, so
+this is a reading): s is the smallest power of two with amax / s <= 448, i.e.
+s = 2^k, k = ceil(log2(amax / 448)) decided exactly, clamped to [-127, 127]
+(the range of an 8-bit biased exponent); v_i / s is then exact and only the
+E4M3 rounding remains.  All-zero tiles keep s = 1.
 """
 from __future__ import annotations
 
@@ -21,34 +28,47 @@ TILE = 128
 F448 = np.float32(448.0)
 
 
-def _scales(amax: np.ndarray) -> np.ndarray:
+def _pow2_scales(amax: np.ndarray) -> np.ndarray:
+    """Smallest 2^k (k in [-127, 127]) with amax <= 448 * 2^k, decided with exact comparisons."""
+    a = amax.astype(np.float64)                   # fp32 values are exact in fp64
+    with np.errstate(divide="ignore"):
+        k = np.ceil(np.log2(np.where(a > 0, a, 1.0) / 448.0)).astype(np.int64)   # estimate
+    k = np.where(a > np.ldexp(448.0, k), k + 1, k)                              # fix the estimate
+    k = np.where(a <= np.ldexp(448.0, k - 1), k - 1, k)                         # both ways
+    k = np.clip(k, -127, 127)
+    return np.where(a == 0, 1.0, np.ldexp(1.0, k)).astype(np.float32)
+
+
+def _scales(amax: np.ndarray, ue8m0: bool = False) -> np.ndarray:
     amax = amax.astype(np.float32)
+    if ue8m0:
+        return _pow2_scales(amax)
     with np.errstate(divide="ignore", invalid="ignore"):
         s = (amax / F448).astype(np.float32)
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 
-def quant_1x128(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quant_1x128(v: np.ndarray, ue8m0: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """v fp32 [rows, cols] (cols % 128 == 0) -> (codes u8 [rows, cols], scales f32 [rows, cols/128])."""
     v = np.asarray(v, dtype=np.float32)
     rows, cols = v.shape
     assert cols % TILE == 0
     tiles = v.reshape(rows, cols // TILE, TILE)
     amax = np.max(np.abs(tiles), axis=-1)
-    s = _scales(amax)
+    s = _scales(amax, ue8m0)
     quot = (tiles / s[..., None]).astype(np.float32)     # fp32 / fp32, IEEE correctly rounded
     codes = e4m3.encode(quot).reshape(rows, cols)
     return codes, s
 
 
-def quant_128x128(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quant_128x128(w: np.ndarray, ue8m0: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """w fp32 [R, C] (both % 128 == 0) -> (codes u8 [R, C], scales f32 [R/128, C/128])."""
     w = np.asarray(w, dtype=np.float32)
     r, c = w.shape
     assert r % TILE == 0 and c % TILE == 0
     blocks = w.reshape(r // TILE, TILE, c // TILE, TILE)
     amax = np.max(np.abs(blocks), axis=(1, 3))
-    s = _scales(amax)
+    s = _scales(amax, ue8m0)
     quot = (blocks / s[:, None, :, None]).astype(np.float32)
     codes = e4m3.encode(quot).reshape(r, c)
     return codes, s

@@ -32,3 +32,21 @@ def test_stored_skew_bias_reproduces_the_profile():
     ld = calibrate.loads(idx, 256)
     assert (ld == 0).sum() >= 16
     assert 12 <= ld.max() / ld.mean() <= 28
+
+
+def test_balancing_update_by_hand():
+    # E = 4, T = 2, k = 4: loads [3, 1, 2, 2], mean 2 -> expert 0 overloaded, 1 underloaded
+    idx = np.array([[0, 0, 1, 2], [0, 2, 3, 3]])
+    bias = np.array([0.5, -0.25, 0.0, 1e-3], np.float32)
+    g = 0.01
+    got = calibrate.update(bias, idx, 4, g)
+    want = np.array([np.float32(0.5) - np.float32(g), np.float32(-0.25) + np.float32(g), 0.0, np.float32(1e-3)],
+                    np.float32)
+    assert np.array_equal(got, want)
+
+
+def test_balancing_update_fractional_mean():
+    # T*k = 6 over E = 4: mean 1.5, so every expert moves (none sits exactly at the mean)
+    idx = np.array([[0, 1, 1], [2, 1, 0]])
+    got = calibrate.update(np.zeros(4, np.float32), idx, 4, 0.5)
+    assert np.array_equal(got, np.array([-0.5, -0.5, 0.5, 0.5], np.float32))   # loads 2, 3, 1, 0

@@ -21,20 +21,20 @@ def tiny():
     return s, x, wr, experts
 
 
-def _dense_masked(s, x, experts, idx, w):
+def _dense_masked(s, x, experts, idx, w, ue8m0=False):
     """Every expert on every token; each output weighted by the token's routing
     weight for that expert, or 0 when the expert was not chosen."""
     from oracle import quant
-    x_q, x_s = quant.quant_1x128(x)
+    x_q, x_s = quant.quant_1x128(x, ue8m0)
     mask = np.zeros((x.shape[0], s.n_experts))
     for t in range(x.shape[0]):
         for j in range(s.top_k):
             mask[t, idx[t, j]] = float(w[t, j])
     out = np.zeros(x.shape, np.float64)
     for e in range(s.n_experts):
-        y = ffn.expert_forward(x_q, x_s, experts[e])["y"]     # per-row quantisation: tokens are independent
+        y = ffn.expert_forward(x_q, x_s, experts[e], ue8m0)["y"]   # per-row quantisation: tokens are independent
         out += mask[:, e:e + 1] * y
-    out += ffn.expert_forward(x_q, x_s, experts[s.n_experts])["y"]
+    out += ffn.expert_forward(x_q, x_s, experts[s.n_experts], ue8m0)["y"]
     return out
 
 
@@ -46,6 +46,25 @@ def test_tiny_layer_equals_dense_masked_evaluation(tiny, bias_scale):
     want = _dense_masked(s, x, experts, r["topk_idx"], r["topk_w"])
     assert np.allclose(r["out_f64"], want, rtol=1e-12, atol=1e-12)
     assert np.array_equal(r["out"], ffn.round_bf16(want))
+
+
+def test_ue8m0_layer_with_prenorm_equals_dense_masked_evaluation(tiny):
+    """The power-of-two-scale variant with the RMSNorm in front: same brute-force pin, on the
+    normalised rows (the router sees them too), with every quantisation power-of-two."""
+    from oracle import norm
+    s, x, wr, _ = tiny
+    experts = [ffn.quantize_expert(*synth.gen_expert_w(s, e), ue8m0=True) for e in range(s.n_experts + 1)]
+    gamma = norm.round_bf16(np.random.default_rng(3).uniform(0.5, 1.5, s.hidden).astype(np.float32))
+    r = ffn.moe_ffn(x, s.n_experts, s.top_k, s.n_group, s.topk_group, lambda e: experts[e], w_router=wr,
+                    ue8m0=True, norm=(gamma, 1e-6))
+    xn = norm.rmsnorm(x, gamma, 1e-6)
+    assert np.array_equal(r["x_norm"], xn)
+    sc = route.sigmoid_scores(route.router_logits(xn, wr))
+    idx, w = route.select(sc, None, s.n_group, s.topk_group, s.top_k)
+    assert np.array_equal(r["topk_idx"], idx)
+    assert np.all(np.frexp(r["x_s"])[0] == 0.5) and np.all(np.frexp(r["h_s"][r["h_s"] > 0])[0] == 0.5)
+    want = _dense_masked(s, xn, experts, idx, w, ue8m0=True)
+    assert np.allclose(r["out_f64"], want, rtol=1e-12, atol=1e-12)
 
 
 def test_given_scores_replace_the_router(tiny):

@@ -118,3 +118,49 @@ def test_128x128_blocks_are_independent_tiles():
     srep = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)
     bound = e4m3.half_ulp(np.abs(w) / srep) * srep * (1 + 2.0 ** -20) + np.abs(w) * 2.0 ** -23
     assert np.all(np.abs(deq - w) <= bound)
+
+
+# ---- power-of-two (UE8M0) scales ----
+
+def test_ue8m0_scale_is_the_smallest_power_of_two_covering_amax():
+    v = _tiles(2)
+    _, s = quant.quant_1x128(v, ue8m0=True)
+    tiles = v.reshape(v.shape[0], -1, 128)
+    for i in range(tiles.shape[0]):
+        for j in range(tiles.shape[1]):
+            amax = Fraction(float(np.max(np.abs(tiles[i, j]))))
+            sc = Fraction(float(s[i, j]))
+            if amax == 0:
+                assert s[i, j] == 1.0
+                continue
+            m, _ = np.frexp(float(s[i, j]))
+            assert m == 0.5                                   # a power of two
+            assert amax <= 448 * sc < 2 * amax                # covers amax, and half of it would not
+
+
+def test_ue8m0_codes_are_the_e4m3_rounding_of_the_exact_quotient():
+    import torch
+    v = _tiles(3)
+    q, s = quant.quant_1x128(v, ue8m0=True)
+    quot = v.reshape(v.shape[0], -1, 128) / s[..., None]       # exact: s is a power of two
+    ref = torch.from_numpy(quot.reshape(v.shape).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(q, ref.numpy())
+
+
+def test_ue8m0_exponent_clamp_and_dequant_bound():
+    v = np.zeros((2, 256), np.float32)
+    v[0, :128] = np.float32(1e-41)                            # amax / 448 below 2^-127: the scale clamps
+    v[1] = np.random.default_rng(4).standard_normal(256).astype(np.float32) * 3
+    q, s = quant.quant_1x128(v, ue8m0=True)
+    assert s[0, 0] == np.float32(2.0 ** -127) and s[0, 1] == 1.0
+    back = quant.dequant_1x128(q, s)
+    half = e4m3.half_ulp(np.abs(v.astype(np.float64)) / np.repeat(s.astype(np.float64), 128, axis=1))
+    assert np.all(np.abs(back[1] - v[1]) <= half[1] * np.repeat(s[1].astype(np.float64), 128) * (1 + 1e-12))
+
+
+def test_ue8m0_weight_blocks():
+    w = np.random.default_rng(6).standard_normal((256, 384)).astype(np.float32) * 0.05
+    q, s = quant.quant_128x128(w, ue8m0=True)
+    blocks = np.abs(w).reshape(2, 128, 3, 128).max(axis=(1, 3)).astype(np.float64)
+    assert np.all(np.frexp(s)[0] == 0.5)
+    assert np.all(blocks <= 448 * s) and np.all(448 * s < 2 * blocks)
