@@ -62,6 +62,11 @@ extern "C" {
 #define MOE_GROUP_SCORE_TOP2_SUM 0     /* sum of the two largest biased scores of the group */
 #define MOE_GROUP_SCORE_MAX 1          /* largest biased score of the group                 */
 
+/* ---- scale formats of the 1x128 / 128x128 quantisation ---- */
+#define MOE_SCALE_F32 0                /* s = fp32(amax / 448), correctly rounded              */
+#define MOE_SCALE_UE8M0 1              /* s = smallest power of two 2^k >= amax / 448, k in
+                                          [-127, 127] (an 8-bit exponent); v / s is then exact */
+
 /* ---- flags ---- */
 #define MOE_ROUTE_SCORES_GIVEN 1       /* moe_route / moe_ffn_forward: `scores` is an input   */
 #define MOE_FWD_DETERMINISTIC 2        /* moe_ffn_forward: slot-ordered combine, no atomics   */
@@ -86,6 +91,9 @@ typedef struct moe_cfg {
   int topk_group;    /* groups kept per token                                              */
   int group_score;   /* MOE_GROUP_SCORE_*                                                  */
   float routed_scale;/* multiplies the normalised routed weights (1.0)                     */
+  int scale_fmt;     /* MOE_SCALE_*: the activation (x and h) scales; the weights' 128x128
+                        scales are expected in the same format                             */
+  float norm_eps;    /* RMSNorm epsilon, used when moe_weights_t.norm_w is given           */
 } moe_cfg_t;
 
 /* Device pointers to one layer's weights.  Expert e's blocks start at
@@ -103,6 +111,7 @@ typedef struct moe_weights {
   const float* sh_w13_s;    /* f32 [2*inter_shared/128][hidden/128]                 */
   const uint8_t* sh_w2_q;   /* e4m3 [hidden][inter_shared]                          */
   const float* sh_w2_s;     /* f32 [hidden/128][inter_shared/128]                   */
+  const uint16_t* norm_w;   /* bf16 [hidden] RMSNorm weight applied to x first, or NULL */
 } moe_weights_t;
 
 /* Extra epilogue operands of fp8_grouped_gemm_blockscaled. */
@@ -110,6 +119,7 @@ typedef struct moe_epi {
   float* h_s;                /* SWIGLU_QUANT: f32 [M][W/128] scales of the output codes      */
   const int32_t* dst_row;    /* WEIGHTED_SCATTER_ADD: destination row of each logical row m */
   const float* row_weight;   /* WEIGHTED_SCATTER_ADD: weight per row m, or NULL (= 1)       */
+  int scale_fmt;             /* SWIGLU_QUANT: MOE_SCALE_* of the output codes' scales        */
 } moe_epi_t;
 
 MOE_API const char* moe_status_string(int status);
@@ -118,18 +128,34 @@ MOE_API const char* moe_last_error(void);
 /* fp8_quant_1x128 - online activation quantisation ([arch blog] "Fine granularity
  * quantization", "Online Quantization").  Per row, per 128 consecutive columns:
  * amax = max |v|; s = fp32(amax / 448) (correctly rounded; 1.0 for an all-zero
- * tile); q = e4m3(fp32(v / s)) rounded to nearest even, saturating.
+ * tile), or with MOE_SCALE_UE8M0 the power of two of MOE_SCALE_UE8M0 ([arch
+ * blog] "More Mantissa bits of fp8": a customised scaling factor);
+ * q = e4m3(fp32(v / s)) rounded to nearest even, saturating.
  *   x      [rows][ld_x] of x_dtype (MOE_DTYPE_BF16 or MOE_DTYPE_F32), cols used
  *   q      e4m3 [rows][ld_q]
  *   s      f32 [rows][cols/128]
  * cols % 128 == 0; ld_x >= cols, ld_q >= cols, rows >= 0 (0: no-op).          */
 MOE_API int fp8_quant_1x128(const void* x, int x_dtype, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
-                    void* stream);
+                    int scale_fmt, void* stream);
 
 /* fp8_quant_128x128 - weight preparation (not on the timed path): the same rule
  * over 128x128 blocks ([aguasto] "Quantization": blockwise FP8).
  *   w f32 [rows][cols] -> q e4m3 [rows][cols], s f32 [rows/128][cols/128].   */
-MOE_API int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, void* stream);
+MOE_API int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, int scale_fmt, void* stream);
+
+/* fp8_rmsnorm_quant_1x128 - the RMSNorm in front of the MLP ([R1 card] facts
+ * table rows "Norm placement" and "Norm type": pre-norm, RMSNorm before the
+ * MLP) fused with fp8_quant_1x128.  Per row t of x:
+ *   inv = fp32(1 / sqrt(S / cols + eps)) in fp64, S = sum of x^2 rounded once to fp64;
+ *   y   = bf16(fp32(fp32(x * inv) * gamma))  (round to nearest even);
+ *   q, s = fp8_quant_1x128 of y with scale_fmt.
+ *   x bf16 [rows][ld_x]; gamma bf16 [cols]; eps >= 0;
+ *   y bf16 [rows][ld_y] or NULL (the normalised rows, e.g. for the router);
+ *   q e4m3 [rows][ld_q]; s f32 [rows][cols/128].
+ * cols % 128 == 0; ld_x, ld_y, ld_q >= cols.                                 */
+MOE_API int fp8_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, float eps, int rows, int cols, int ld_x,
+                                    uint16_t* y, int ld_y, uint8_t* q, int ld_q, float* s, int scale_fmt,
+                                    void* stream);
 
 /* moe_pack_weights - reorders row-major e4m3 weights [G][N][K] into the
  * MFMA-fragment order every GEMM of this library reads (offline, like the
@@ -158,6 +184,17 @@ MOE_API int moe_pack_weights(const uint8_t* src, int G, int N, int K, uint8_t* d
  * n_experts / n_group, n_experts <= 1024, n_group <= 64, top_k <= 64.          */
 MOE_API int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, const moe_cfg_t* cfg,
               float* scores, int flags, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* moe_bias_update - one balancing step of the routing-only bias ([arch blog]
+ * "Local Balanced Routing to Experts": the bias of an overloaded expert is
+ * decreased by gamma, that of an underloaded one increased).  With load_e the
+ * number of entries of topk_idx equal to e and the mean load (T*k)/E:
+ *   bias[e] = fp32(bias[e] + gamma * sign(mean - load_e))   (+0 at the mean)
+ *   topk_idx i32 [T][k] (entries outside [0, E) are not counted); bias f32 [E]
+ *   in place; counts i32 [E] receives load_e, or NULL.
+ * 1 <= E <= 1024, T >= 0, k >= 1, T*k <= 2^30.                               */
+MOE_API int moe_bias_update(const int32_t* topk_idx, int T, int k, int E, float gamma, float* bias, int32_t* counts,
+                            void* stream);
 
 /* moe_permute - sort the T*k assignments a = t*k + j by expert, stably (by
  * expert, then a).  offsets[e]..offsets[e+1] is expert e's range of sorted
@@ -206,6 +243,9 @@ MOE_API size_t moe_ffn_workspace_size(int T, const moe_cfg_t* cfg);
  *   per expert h = silu(x W_gate^T) * (x W_up^T) -> 1x128 e4m3; y = h W_down^T;
  *   out[t] = bf16(sum_j topk_w[t][j] * y[t][j] + y_shared[t]).
  * n_experts == 0 runs the dense gated FFN (x -> shared MLP -> out).
+ * With w->norm_w, x first goes through the RMSNorm of fp8_rmsnorm_quant_1x128
+ * (cfg->norm_eps) and the router and the experts see the normalised rows.
+ * cfg->scale_fmt selects the activation scale format (x and h).
  *   x bf16 [T][hidden]; out bf16 [T][hidden];
  *   scores f32 [T][E], topk_idx i32 [T][k], topk_w f32 [T][k]: optional outputs
  *   (NULL to skip); with MOE_ROUTE_SCORES_GIVEN `scores` is an input instead.

@@ -11,11 +11,18 @@ The pages name the norm but give no formula, precision or epsilon.  Reading
   inv_t = fp32( 1 / sqrt( (sum_i x_ti^2) / d + eps ) )   computed in fp64
   y_ti  = bf16( fp32( fp32(x_ti * inv_t) * gamma_i ) )   two fp32 products, one bf16 rounding
 
+The sum of squares is the exact sum rounded once to fp64 (squares of bf16
+values are exact; math.fsum sums exactly), so it does not depend on the order
+of the additions; the division, the square root and the reciprocal are IEEE
+fp64 operations.
+
 x and gamma are bf16 values, eps an fp32 value.  y (bf16) is what the layer
 hands on: the router reads it and fp8_quant_1x128 quantises it, so the fused
 kernel's codes and scales are quant_1x128(y).
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -31,7 +38,7 @@ def inv_rms(x: np.ndarray, eps: float) -> np.ndarray:
     """Per-row fp32 1/RMS of bf16-valued rows x [T, d]."""
     x64 = np.asarray(x, dtype=np.float64)
     d = x64.shape[1]
-    ss = np.sum(x64 * x64, axis=1)                     # squares of bf16 values are exact in fp64
+    ss = np.array([math.fsum(r) for r in x64 * x64])   # exact squares, exactly summed, rounded once
     e64 = float(np.float32(eps))
     return (1.0 / np.sqrt(ss / d + e64)).astype(np.float32)
 

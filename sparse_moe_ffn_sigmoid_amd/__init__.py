@@ -6,8 +6,9 @@ and raises MoeError on a non-zero status.  Every step of the layer runs in the
 library's HIP kernels; there is no fallback when the library is missing.
 
 Calls (same names as the C ABI in include/moefp8.h):
-    fp8_quant_1x128, fp8_quant_128x128, moe_pack_weights, moe_route, moe_permute,
-    moe_unpermute, fp8_grouped_gemm_blockscaled, moe_ffn_workspace_size, moe_ffn_forward
+    fp8_quant_1x128, fp8_quant_128x128, fp8_rmsnorm_quant_1x128, moe_pack_weights, moe_route,
+    moe_bias_update, moe_permute, moe_unpermute, fp8_grouped_gemm_blockscaled, moe_ffn_workspace_size,
+    moe_ffn_forward
 """
 from __future__ import annotations
 
@@ -19,7 +20,11 @@ import torch
 from . import _lib
 from ._lib import (MOE_EPI_STORE_BF16, MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_QUANT,  # noqa: F401
                    MOE_EPI_WEIGHTED_SCATTER_ADD, MOE_FWD_DETERMINISTIC, MOE_GROUP_SCORE_MAX,
-                   MOE_GROUP_SCORE_TOP2_SUM, MOE_ROUTE_SCORES_GIVEN)
+                   MOE_GROUP_SCORE_TOP2_SUM, MOE_ROUTE_SCORES_GIVEN, MOE_SCALE_F32, MOE_SCALE_UE8M0)
+
+
+def _fmt(ue8m0: bool) -> int:
+    return MOE_SCALE_UE8M0 if ue8m0 else MOE_SCALE_F32
 
 
 class MoeError(RuntimeError):
@@ -61,16 +66,19 @@ class MoeConfig:
     topk_group: int
     group_score: int = MOE_GROUP_SCORE_TOP2_SUM
     routed_scale: float = 1.0
+    ue8m0: bool = False                 # power-of-two activation scales (weights quantised the same way)
+    norm_eps: float = 1e-6              # RMSNorm epsilon, used when MoeWeights.norm_w is set
 
     def c(self) -> _lib.MoeCfgC:
         return _lib.MoeCfgC(self.hidden, self.inter, self.n_experts, self.top_k, self.n_shared, self.inter_shared,
-                            self.n_group, self.topk_group, self.group_score, self.routed_scale)
+                            self.n_group, self.topk_group, self.group_score, self.routed_scale, _fmt(self.ue8m0),
+                            self.norm_eps)
 
     @staticmethod
-    def of(shape) -> "MoeConfig":
+    def of(shape, **kw) -> "MoeConfig":
         """From any object with the layer's shape fields (hidden, inter, n_experts, ...)."""
         return MoeConfig(shape.hidden, shape.inter, shape.n_experts, shape.top_k, shape.n_shared, shape.inter_shared,
-                         shape.n_group, shape.topk_group, MOE_GROUP_SCORE_TOP2_SUM, float(shape.routed_scale))
+                         shape.n_group, shape.topk_group, MOE_GROUP_SCORE_TOP2_SUM, float(shape.routed_scale), **kw)
 
 
 @dataclasses.dataclass
@@ -86,14 +94,17 @@ class MoeWeights:
     sh_w2_s: torch.Tensor | None = None
     w_router: torch.Tensor | None = None
     bias: torch.Tensor | None = None
+    norm_w: torch.Tensor | None = None   # bf16 [hidden]: RMSNorm applied to x first
 
     def c(self) -> _lib.MoeWeightsC:
         f = {n: (None if getattr(self, n) is None else getattr(self, n).data_ptr()) for n in
-             ("w_router", "bias", "w13_q", "w13_s", "w2_q", "w2_s", "sh_w13_q", "sh_w13_s", "sh_w2_q", "sh_w2_s")}
+             ("w_router", "bias", "w13_q", "w13_s", "w2_q", "w2_s", "sh_w13_q", "sh_w13_s", "sh_w2_q", "sh_w2_s",
+              "norm_w")}
         return _lib.MoeWeightsC(**f)
 
 
-def fp8_quant_1x128(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+def fp8_quant_1x128(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                    ue8m0: bool = False):
     """x [rows, cols] bf16 or fp32 -> (codes uint8 [rows, cols], scales fp32 [rows, cols/128])."""
     _dev(x, "x")
     rows, cols = x.shape
@@ -102,11 +113,13 @@ def fp8_quant_1x128(x: torch.Tensor, q: torch.Tensor | None = None, s: torch.Ten
         raise ValueError("x must be bfloat16 or float32")
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((rows, max(cols // 128, 0)), dtype=torch.float32, device=x.device) if s is None else s
-    _check("fp8_quant_1x128", _lib.load().fp8_quant_1x128(_p(x), dt, rows, cols, cols, _p(q), cols, _p(s), _stream(x)))
+    _check("fp8_quant_1x128", _lib.load().fp8_quant_1x128(_p(x), dt, rows, cols, cols, _p(q), cols, _p(s),
+                                                          _fmt(ue8m0), _stream(x)))
     return q, s
 
 
-def fp8_quant_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+def fp8_quant_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                      ue8m0: bool = False):
     """w [rows, cols] fp32 -> (codes uint8 [rows, cols], scales fp32 [rows/128, cols/128])."""
     _dev(w, "w")
     rows, cols = w.shape
@@ -114,8 +127,37 @@ def fp8_quant_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.T
         raise ValueError("w must be float32")
     q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device) if q is None else q
     s = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=w.device) if s is None else s
-    _check("fp8_quant_128x128", _lib.load().fp8_quant_128x128(_p(w), rows, cols, _p(q), _p(s), _stream(w)))
+    _check("fp8_quant_128x128", _lib.load().fp8_quant_128x128(_p(w), rows, cols, _p(q), _p(s), _fmt(ue8m0),
+                                                              _stream(w)))
     return q, s
+
+
+def fp8_rmsnorm_quant_1x128(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, want_y: bool = True,
+                            ue8m0: bool = False):
+    """x bf16 [rows, cols], gamma bf16 [cols] -> (y bf16 [rows, cols] or None, codes uint8, scales fp32)."""
+    _dev(x, "x")
+    _dev(gamma, "gamma")
+    if x.dtype != torch.bfloat16 or gamma.dtype != torch.bfloat16:
+        raise ValueError("x and gamma must be bfloat16")
+    rows, cols = x.shape
+    y = torch.empty_like(x) if want_y else None
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows, max(cols // 128, 0)), dtype=torch.float32, device=x.device)
+    _check("fp8_rmsnorm_quant_1x128", _lib.load().fp8_rmsnorm_quant_1x128(
+        _p(x), _p(gamma), eps, rows, cols, cols, _p(y), cols, _p(q), cols, _p(s), _fmt(ue8m0), _stream(x)))
+    return y, q, s
+
+
+def moe_bias_update(topk_idx: torch.Tensor, n_experts: int, gamma: float, bias: torch.Tensor,
+                    counts: torch.Tensor | None = None) -> torch.Tensor | None:
+    """In place: bias[e] += gamma * sign(mean load - load_e) from int32 topk_idx [T, k].  Fills and
+    returns ``counts`` (int32 [E]) when given."""
+    _dev(topk_idx, "topk_idx")
+    _dev(bias, "bias")
+    T, k = topk_idx.shape
+    _check("moe_bias_update", _lib.load().moe_bias_update(_p(topk_idx), T, k, n_experts, gamma, _p(bias), _p(counts),
+                                                          _stream(bias)))
+    return counts
 
 
 def moe_pack_weights(w_q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -128,10 +170,11 @@ def moe_pack_weights(w_q: torch.Tensor, out: torch.Tensor | None = None) -> torc
     return out
 
 
-def quantize_pack_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+def quantize_pack_128x128(w: torch.Tensor, q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                          ue8m0: bool = False):
     """fp32 weights [N, K] -> (packed e4m3 codes [N, K], scales [N/128, K/128]): fp8_quant_128x128
     followed by moe_pack_weights (a temporary holds the row-major codes)."""
-    rm, s = fp8_quant_128x128(w, s=s)
+    rm, s = fp8_quant_128x128(w, s=s, ue8m0=ue8m0)
     return moe_pack_weights(rm, out=q), s
 
 
@@ -193,7 +236,8 @@ def moe_unpermute(y_sorted: torch.Tensor, assign_pos: torch.Tensor, top_k: int, 
 
 
 def fp8_grouped_gemm_blockscaled(a_q, a_s, b_q, b_s, offsets, epilogue: int, a_gather=None, m_max: int | None = None,
-                                 out=None, h_s=None, dst_row=None, row_weight=None, out_rows: int | None = None):
+                                 out=None, h_s=None, dst_row=None, row_weight=None, out_rows: int | None = None,
+                                 ue8m0: bool = False):
     """Grouped block-scaled GEMM (see the C header).  b_q uint8 [G, N, K].  Returns the output
     tensor (and h_s for MOE_EPI_SWIGLU_QUANT)."""
     G, N, K = b_q.shape
@@ -211,7 +255,7 @@ def fp8_grouped_gemm_blockscaled(a_q, a_s, b_q, b_s, offsets, epilogue: int, a_g
     if epilogue == MOE_EPI_SWIGLU_QUANT and h_s is None:
         h_s = torch.empty((M, N // 256), dtype=torch.float32, device=dev)
     epi = _lib.MoeEpiC(None if h_s is None else h_s.data_ptr(), None if dst_row is None else dst_row.data_ptr(),
-                       None if row_weight is None else row_weight.data_ptr())
+                       None if row_weight is None else row_weight.data_ptr(), _fmt(ue8m0))
     _check("fp8_grouped_gemm_blockscaled", _lib.load().fp8_grouped_gemm_blockscaled(
         _p(a_q), _p(a_s), _p(a_gather), _p(b_q), _p(b_s), _p(offsets), G, M, N, K, epilogue, ctypes.byref(epi),
         _p(out), _stream(a_q)))

@@ -13,6 +13,7 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_U8 = 0, 1, 2
+MOE_SCALE_F32, MOE_SCALE_UE8M0 = 0, 1
 MOE_GROUP_SCORE_TOP2_SUM, MOE_GROUP_SCORE_MAX = 0, 1
 MOE_ROUTE_SCORES_GIVEN = 1
 MOE_FWD_DETERMINISTIC = 2
@@ -20,7 +21,8 @@ MOE_EPI_STORE_F32, MOE_EPI_STORE_BF16, MOE_EPI_SWIGLU_QUANT, MOE_EPI_WEIGHTED_SC
 
 EXPORTED = ("moe_status_string", "moe_last_error", "fp8_quant_1x128", "fp8_quant_128x128", "moe_route",
             "moe_permute_workspace_size", "moe_permute", "moe_unpermute", "fp8_grouped_gemm_blockscaled",
-            "moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_stages", "moe_pack_weights")
+            "moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_stages", "moe_pack_weights",
+            "fp8_rmsnorm_quant_1x128", "moe_bias_update")
 MOE_FWD_STAGE_EVENTS = 6
 
 
@@ -28,16 +30,17 @@ class MoeCfgC(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int), ("inter", ctypes.c_int), ("n_experts", ctypes.c_int),
                 ("top_k", ctypes.c_int), ("n_shared", ctypes.c_int), ("inter_shared", ctypes.c_int),
                 ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int), ("group_score", ctypes.c_int),
-                ("routed_scale", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("scale_fmt", ctypes.c_int), ("norm_eps", ctypes.c_float)]
 
 
 class MoeWeightsC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "bias", "w13_q", "w13_s", "w2_q", "w2_s",
-                                                "sh_w13_q", "sh_w13_s", "sh_w2_q", "sh_w2_s")]
+                                                "sh_w13_q", "sh_w13_s", "sh_w2_q", "sh_w2_s", "norm_w")]
 
 
 class MoeEpiC(ctypes.Structure):
-    _fields_ = [("h_s", ctypes.c_void_p), ("dst_row", ctypes.c_void_p), ("row_weight", ctypes.c_void_p)]
+    _fields_ = [("h_s", ctypes.c_void_p), ("dst_row", ctypes.c_void_p), ("row_weight", ctypes.c_void_p),
+                ("scale_fmt", ctypes.c_int)]
 
 
 _lib = None
@@ -56,8 +59,10 @@ def load() -> ctypes.CDLL:
     sig = {
         "moe_status_string": (ctypes.c_char_p, [i]),
         "moe_last_error": (ctypes.c_char_p, []),
-        "fp8_quant_1x128": (i, [vp, i, i, i, i, vp, i, vp, vp]),
-        "fp8_quant_128x128": (i, [vp, i, i, vp, vp, vp]),
+        "fp8_quant_1x128": (i, [vp, i, i, i, i, vp, i, vp, i, vp]),
+        "fp8_quant_128x128": (i, [vp, i, i, vp, vp, i, vp]),
+        "fp8_rmsnorm_quant_1x128": (i, [vp, vp, ctypes.c_float, i, i, i, vp, i, vp, i, vp, i, vp]),
+        "moe_bias_update": (i, [vp, i, i, i, ctypes.c_float, vp, vp, vp]),
         "moe_pack_weights": (i, [vp, i, i, i, vp, vp]),
         "moe_route": (i, [vp, vp, vp, i, ctypes.POINTER(MoeCfgC), vp, i, vp, vp, vp]),
         "moe_permute_workspace_size": (sz, [i, i, i]),

@@ -67,6 +67,10 @@ int check_route_cfg(const moe_cfg_t* c) {
 
 int check_layer_cfg(const moe_cfg_t* c) {
   REQUIRE(c, MOE_ERR_INVALID_ARG, "cfg is NULL");
+  REQUIRE(c->scale_fmt == MOE_SCALE_F32 || c->scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG,
+          "scale_fmt %d unknown", c->scale_fmt);
+  REQUIRE(c->norm_eps >= 0.0f && c->norm_eps < 3.0e38f, MOE_ERR_INVALID_ARG, "norm_eps %g not finite and >= 0",
+          (double)c->norm_eps);
   REQUIRE(c->hidden > 0 && c->hidden % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d not a positive multiple of 128",
           c->hidden);
   REQUIRE(c->n_shared == 0 || c->n_shared == 1, MOE_ERR_UNSUPPORTED_SHAPE, "n_shared %d not 0 or 1", c->n_shared);
@@ -91,7 +95,7 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Workspace layout of moe_ffn_forward (offsets from ws, 256-byte aligned).
 struct FwdLayout {
-  size_t x_q, x_s, scores, topk_idx, topk_w, offsets, sorted_assign, assign_pos, sorted_token, sorted_w, perm_scratch,
+  size_t x_norm, x_q, x_s, scores, topk_idx, topk_w, offsets, sorted_assign, assign_pos, sorted_token, sorted_w, perm_scratch,
       h_q, h_s, hs_q, hs_s, y_sorted, y_shared, total;
 };
 
@@ -106,6 +110,7 @@ FwdLayout fwd_layout(int T, const moe_cfg_t* c) {
   const size_t t = (size_t)T, d = (size_t)c->hidden;
   const size_t E = (size_t)c->n_experts, k = (size_t)(c->n_experts ? c->top_k : 0);
   const size_t n = t * k;
+  L.x_norm = take(t * d * 2);                    // bf16 rows after the optional RMSNorm
   L.x_q = take(t * d);
   L.x_s = take(t * (d / 128) * 4);
   L.scores = take(t * E * 4);
@@ -150,9 +155,11 @@ const char* moe_status_string(int status) {
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 int fp8_quant_1x128(const void* x, int x_dtype, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
-                    void* stream) {
+                    int scale_fmt, void* stream) {
   REQUIRE(x_dtype == MOE_DTYPE_BF16 || x_dtype == MOE_DTYPE_F32, MOE_ERR_INVALID_ARG, "x_dtype %d not BF16/F32",
           x_dtype);
+  REQUIRE(scale_fmt == MOE_SCALE_F32 || scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG, "scale_fmt %d unknown",
+          scale_fmt);
   REQUIRE(rows >= 0, MOE_ERR_INVALID_ARG, "rows %d < 0", rows);
   REQUIRE(cols > 0 && cols % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "cols %d not a positive multiple of 128", cols);
   REQUIRE(ld_x >= cols && ld_q >= cols, MOE_ERR_INVALID_ARG, "ld_x %d / ld_q %d smaller than cols %d", ld_x, ld_q,
@@ -162,19 +169,56 @@ int fp8_quant_1x128(const void* x, int x_dtype, int rows, int cols, int ld_x, ui
   const int esz = x_dtype == MOE_DTYPE_BF16 ? 2 : 4;
   REQUIRE(aligned(x, 16) && ((size_t)ld_x * esz) % 16 == 0, MOE_ERR_INVALID_ARG, "x rows not 16-byte aligned");
   REQUIRE(aligned(q, 16) && ld_q % 16 == 0 && aligned(s, 4), MOE_ERR_INVALID_ARG, "q/s not aligned");
-  HIP_TRY(launch_quant_1x128(x, x_dtype == MOE_DTYPE_BF16, rows, cols, ld_x, q, ld_q, s, (hipStream_t)stream),
+  HIP_TRY(launch_quant_1x128(x, x_dtype == MOE_DTYPE_BF16, rows, cols, ld_x, q, ld_q, s, scale_fmt == MOE_SCALE_UE8M0,
+                             (hipStream_t)stream),
           "fp8_quant_1x128");
   return ok();
 }
 
-int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, void* stream) {
+int fp8_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, int scale_fmt, void* stream) {
+  REQUIRE(scale_fmt == MOE_SCALE_F32 || scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG, "scale_fmt %d unknown",
+          scale_fmt);
   REQUIRE(rows >= 0 && cols >= 0, MOE_ERR_INVALID_ARG, "negative size");
   REQUIRE(rows % 128 == 0 && cols % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "rows %d / cols %d not multiples of 128",
           rows, cols);
   if (rows == 0 || cols == 0) return ok();
   REQUIRE(w && q && s, MOE_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(s, 4), MOE_ERR_INVALID_ARG, "pointer not aligned");
-  HIP_TRY(launch_quant_128x128(w, rows, cols, q, s, (hipStream_t)stream), "fp8_quant_128x128");
+  HIP_TRY(launch_quant_128x128(w, rows, cols, q, s, scale_fmt == MOE_SCALE_UE8M0, (hipStream_t)stream),
+          "fp8_quant_128x128");
+  return ok();
+}
+
+int fp8_rmsnorm_quant_1x128(const uint16_t* x, const uint16_t* gamma, float eps, int rows, int cols, int ld_x,
+                            uint16_t* y, int ld_y, uint8_t* q, int ld_q, float* s, int scale_fmt, void* stream) {
+  REQUIRE(scale_fmt == MOE_SCALE_F32 || scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG, "scale_fmt %d unknown",
+          scale_fmt);
+  REQUIRE(rows >= 0, MOE_ERR_INVALID_ARG, "rows %d < 0", rows);
+  REQUIRE(cols > 0 && cols % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "cols %d not a positive multiple of 128", cols);
+  REQUIRE(eps >= 0.0f && eps < 3.0e38f, MOE_ERR_INVALID_ARG, "eps %g not finite and >= 0", (double)eps);
+  REQUIRE(ld_x >= cols && ld_q >= cols && (!y || ld_y >= cols), MOE_ERR_INVALID_ARG,
+          "leading dimensions smaller than cols %d", cols);
+  if (rows == 0) return ok();
+  REQUIRE(x && gamma && q && s, MOE_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned(x, 16) && ld_x % 8 == 0 && aligned(gamma, 16) && (!y || (aligned(y, 16) && ld_y % 8 == 0)),
+          MOE_ERR_INVALID_ARG, "x / gamma / y rows not 16-byte aligned");
+  REQUIRE(aligned(q, 16) && ld_q % 16 == 0 && aligned(s, 4), MOE_ERR_INVALID_ARG, "q/s not aligned");
+  HIP_TRY(launch_rmsnorm_quant(x, gamma, eps, rows, cols, ld_x, y, ld_y, q, ld_q, s, scale_fmt == MOE_SCALE_UE8M0,
+                               (hipStream_t)stream),
+          "fp8_rmsnorm_quant_1x128");
+  return ok();
+}
+
+int moe_bias_update(const int32_t* topk_idx, int T, int k, int E, float gamma, float* bias, int32_t* counts,
+                    void* stream) {
+  REQUIRE(T >= 0 && k >= 1, MOE_ERR_INVALID_ARG, "T %d, k %d", T, k);
+  REQUIRE(E >= 1 && E <= 1024, MOE_ERR_UNSUPPORTED_SHAPE, "E %d not in [1, 1024]", E);
+  REQUIRE((long)T * k <= (1l << 30), MOE_ERR_UNSUPPORTED_SHAPE, "T*k too large");
+  REQUIRE(gamma == gamma && gamma > -3.0e38f && gamma < 3.0e38f, MOE_ERR_INVALID_ARG, "gamma not finite");
+  REQUIRE(bias && (T == 0 || topk_idx), MOE_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned(bias, 4) && (!counts || aligned(counts, 4)) && (!topk_idx || aligned(topk_idx, 4)),
+          MOE_ERR_INVALID_ARG, "pointer not aligned");
+  HIP_TRY(launch_bias_update(topk_idx, (long)T * k, E, gamma, bias, counts, (hipStream_t)stream), "moe_bias_update");
   return ok();
 }
 
@@ -283,8 +327,11 @@ int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int
   sg.K = K;
   sg.out = out;
   if (epilogue == MOE_EPI_SWIGLU_QUANT) {
+    REQUIRE(epi->scale_fmt == MOE_SCALE_F32 || epi->scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG,
+            "epi->scale_fmt %d unknown", epi->scale_fmt);
     sg.out_s = epi->h_s;
     sg.ld_out = N / 2;
+    sg.pow2_scales = epi->scale_fmt == MOE_SCALE_UE8M0;
   } else {
     sg.ld_out = N;
   }
@@ -343,6 +390,7 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
   }
   if (cfg->n_shared)
     REQUIRE(w->sh_w13_q && w->sh_w13_s && w->sh_w2_q && w->sh_w2_s, MOE_ERR_INVALID_ARG, "NULL shared weights");
+  REQUIRE(!w->norm_w || aligned(w->norm_w, 16), MOE_ERR_INVALID_ARG, "norm_w not 16-byte aligned");
   const FwdLayout L = fwd_layout(T, cfg);
   REQUIRE(ws && aligned(ws, 256) && ws_bytes >= L.total, MOE_ERR_WORKSPACE,
           "workspace %zu bytes (needs %zu, 256-byte aligned)", ws_bytes, L.total);
@@ -357,8 +405,17 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
   const int W = cfg->inter, Ws = cfg->inter_shared;
   uint8_t* x_q = at(L.x_q);
   float* x_s = reinterpret_cast<float*>(at(L.x_s));
+  const bool pow2 = cfg->scale_fmt == MOE_SCALE_UE8M0;
+  const uint16_t* xin = x;                      // the rows the router reads
   HIP_TRY(mark(0), "event");
-  HIP_TRY(launch_quant_1x128(x, true, T, d, d, x_q, d, x_s, s), "quantize x");
+  if (w->norm_w) {
+    uint16_t* x_norm = reinterpret_cast<uint16_t*>(at(L.x_norm));
+    HIP_TRY(launch_rmsnorm_quant(x, w->norm_w, cfg->norm_eps, T, d, d, x_norm, d, x_q, d, x_s, pow2, s),
+            "RMSNorm + quantize x");
+    xin = x_norm;
+  } else {
+    HIP_TRY(launch_quant_1x128(x, true, T, d, d, x_q, d, x_s, pow2, s), "quantize x");
+  }
   HIP_TRY(mark(1), "event");
 
   int32_t* sorted_token = reinterpret_cast<int32_t*>(at(L.sorted_token));
@@ -371,7 +428,7 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
   if (routed) {
     float* sc = scores ? scores : reinterpret_cast<float*>(at(L.scores));
     int32_t* ti = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(L.topk_idx));
-    if (!(flags & MOE_ROUTE_SCORES_GIVEN)) HIP_TRY(launch_router(x, w->w_router, T, E, d, sc, s), "router");
+    if (!(flags & MOE_ROUTE_SCORES_GIVEN)) HIP_TRY(launch_router(xin, w->w_router, T, E, d, sc, s), "router");
     HIP_TRY(launch_route(sc, w->bias, T, E, k, cfg->n_group, cfg->topk_group, cfg->group_score, cfg->routed_scale, ti,
                          tw, s),
             "route");
@@ -403,6 +460,7 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
     g0.out = hs_q;
     g0.out_s = hs_s;
     g0.ld_out = Ws;
+    g0.pow2_scales = pow2;
   }
   if (routed) {
     GemmSeg& g1 = up.seg[1];
@@ -421,6 +479,7 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
     g1.out = h_q;
     g1.out_s = h_s;
     g1.ld_out = W;
+    g1.pow2_scales = pow2;
   }
   HIP_TRY(launch_grouped_gemm(up, kEpiSwiglu, bm, s), "gate/up GEMM");
   HIP_TRY(mark(3), "event");

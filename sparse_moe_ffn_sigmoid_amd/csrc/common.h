@@ -40,6 +40,27 @@ __device__ __forceinline__ uint32_t e4m3_encode(float f) {
   return code | sign;
 }
 
+// Scale of one quantisation tile (amax >= 0): fp32(amax / 448), correctly rounded; or, with
+// pow2 (power-of-two "UE8M0" scales), the smallest 2^k, k in [-127, 127], with amax <= 448 * 2^k.
+// For amax = m * 2^E (m in [1, 2)), 448 * 2^k = 1.75 * 2^(k + 8) covers amax exactly when
+// k >= E - 8, or k >= E - 7 when m > 1.75; subnormal amax takes the clamp.  1 for amax == 0.
+__device__ __forceinline__ float tile_scale(float amax, bool pow2) {
+  if (amax == 0.0f) return 1.0f;
+  if (!pow2) return amax / 448.0f;
+  const uint32_t b = __float_as_uint(amax);
+  const int ef = (int)(b >> 23);
+  int k = ef == 0 ? -127 : ef - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  k = k < -127 ? -127 : (k > 127 ? 127 : k);
+  return k >= -126 ? __uint_as_float((uint32_t)(k + 127) << 23) : __uint_as_float(0x400000u);   // 2^-127: subnormal
+}
+
+// Error-free sum (Knuth's TwoSum): s + e == a + b exactly, s = fl(a + b).
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

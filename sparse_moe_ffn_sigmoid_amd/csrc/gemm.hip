@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * q + i;
       const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-      const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+      const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
 #pragma unroll
       for (int j = 0; j < NTW; ++j) stage[r * 128 + wave * CW + 16 * j + r16] = (uint8_t)e4m3_encode(h[j][i] / sc);
       if (wave == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + (nbase >> 7)] = sc;
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
         float amax = red[0][r];
 #pragma unroll
         for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[w2][r]);
-        const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+        const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
 #pragma unroll
         for (int j = 0; j < H; ++j)
           stage[r * 128 + wn * 16 * H + 16 * j + r16] = (uint8_t)e4m3_encode(h[mi][j][i] / sc);

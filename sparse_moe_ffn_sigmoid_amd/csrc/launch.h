@@ -31,6 +31,7 @@ struct GemmSeg {
   int ld_out;                // elements per output row
   const int32_t* dst_row;    // scatter: destination row per logical row (nullptr = identity)
   const float* row_w;        // scatter: weight per logical row (nullptr = 1)
+  int pow2_scales;           // SwiGLU requantisation: power-of-two (UE8M0) scales when nonzero
 };
 
 struct GemmArgs {
@@ -38,8 +39,12 @@ struct GemmArgs {
 };
 
 hipError_t launch_quant_1x128(const void* x, bool bf16, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
+                              bool pow2, hipStream_t st);
+hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, bool pow2, hipStream_t st);
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int rows, int cols, int ld_x,
+                                uint16_t* y, int ld_y, uint8_t* q, int ld_q, float* s, bool pow2, hipStream_t st);
+hipError_t launch_bias_update(const int32_t* topk_idx, long n, int E, float gamma, float* bias, int32_t* counts,
                               hipStream_t st);
-hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_pack(const uint8_t* src, int G, int N, int K, uint8_t* dst, hipStream_t st);
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, hipStream_t st);
 hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,

@@ -320,3 +320,38 @@ hipError_t launch_fill_zero(float* p, long n, hipStream_t st) {
 }
 
 }  // namespace moefp8
+
+namespace moefp8 {
+
+// Routing-bias balancing step (onlylabs "DeepSeek v3 and R1 Model Architecture",
+// "Local Balanced Routing to Experts": an overloaded expert's bias goes down by
+// gamma, an underloaded one's goes up).  One workgroup: the n = T*k expert ids
+// are counted in LDS (integer atomics: exact), then, against the mean load
+// n / E, bias[e] += gamma * sign(n - E * load_e) in fp32 (an expert exactly at
+// the mean adds +0).  Ids outside [0, E) are not counted.
+__global__ __launch_bounds__(1024) void bias_update_kernel(const int32_t* __restrict__ idx, long n, int E, float gamma,
+                                                           float* __restrict__ bias, int32_t* __restrict__ counts) {
+  __shared__ int cnt[1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  for (long i = tid; i < n; i += 1024) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    const long diff = n - (long)E * cnt[e];
+    const float step = diff > 0 ? gamma : (diff < 0 ? -gamma : 0.0f);
+    bias[e] = bias[e] + step;
+    if (counts) counts[e] = cnt[e];
+  }
+}
+
+hipError_t launch_bias_update(const int32_t* topk_idx, long n, int E, float gamma, float* bias, int32_t* counts,
+                              hipStream_t st) {
+  bias_update_kernel<<<1, 1024, 0, st>>>(topk_idx, n, E, gamma, bias, counts);
+  return hipGetLastError();
+}
+
+}  // namespace moefp8

@@ -13,7 +13,8 @@ namespace moefp8 {
 // (one 16-byte load for bf16, two for fp32; one 8-byte store of codes).
 template <bool kBf16>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int rows, int cols, int ld_x,
-                                                          uint8_t* __restrict__ q, int ld_q, float* __restrict__ s) {
+                                                          uint8_t* __restrict__ q, int ld_q, float* __restrict__ s,
+                                                          int pow2) {
   const int tpr = cols >> 7;
   const long ntiles = (long)rows * tpr;
   const long tile = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = group_max<16>(amax);
-  const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+  const float sc = tile_scale(amax, pow2 != 0);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / sc) << (8 * i);
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
 // One workgroup per 128x128 block; thread t holds row t/2, columns (t%2)*64 .. +64;
 // the block's amax is reduced per wave, then across the 4 waves through LDS.
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restrict__ w, int rows, int cols,
-                                                            uint8_t* __restrict__ q, float* __restrict__ s) {
+                                                            uint8_t* __restrict__ q, float* __restrict__ s, int pow2) {
   __shared__ float red[4];
   const int bc = blockIdx.x, br = blockIdx.y;
   const int tid = threadIdx.x;
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = amax == 0.0f ? 1.0f : amax / 448.0f;
+  const float sc = tile_scale(amax, pow2 != 0);
   uint8_t* dst = q + (long)(br * 128 + rr) * cols + bc * 128 + cc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -127,21 +128,128 @@ hipError_t launch_pack(const uint8_t* src, int G, int N, int K, uint8_t* dst, hi
 }
 
 hipError_t launch_quant_1x128(const void* x, bool bf16, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
-                              hipStream_t st) {
+                              bool pow2, hipStream_t st) {
   const long ntiles = (long)rows * (cols / 128);
   if (ntiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)((ntiles + 15) / 16);
   if (bf16)
-    quant_1x128_kernel<true><<<grid, 256, 0, st>>>(x, rows, cols, ld_x, q, ld_q, s);
+    quant_1x128_kernel<true><<<grid, 256, 0, st>>>(x, rows, cols, ld_x, q, ld_q, s, pow2);
   else
-    quant_1x128_kernel<false><<<grid, 256, 0, st>>>(x, rows, cols, ld_x, q, ld_q, s);
+    quant_1x128_kernel<false><<<grid, 256, 0, st>>>(x, rows, cols, ld_x, q, ld_q, s, pow2);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, hipStream_t st) {
+hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, float* s, bool pow2, hipStream_t st) {
   if (rows == 0 || cols == 0) return hipSuccess;
   dim3 grid(cols / 128, rows / 128);
-  quant_128x128_kernel<<<grid, 256, 0, st>>>(w, rows, cols, q, s);
+  quant_128x128_kernel<<<grid, 256, 0, st>>>(w, rows, cols, q, s, pow2);
+  return hipGetLastError();
+}
+
+// RMSNorm fused with the 1x128 quantisation (llm-architectures-explained,
+// "DeepSeek-R1", facts rows "Norm placement" / "Norm type": RMSNorm right before
+// the MLP).  One workgroup per row:
+//   pass 1: the sum of squares.  Squares of bf16 values are exact in fp64; they
+//     are accumulated in double-double (TwoSum) per lane and reduced pairwise,
+//     then rounded once, which gives the exactly rounded fp64 sum for any
+//     realistic row (so the result does not depend on the summation order);
+//   inv = fp32(1 / sqrt(sum / cols + eps)) in fp64;
+//   pass 2 (the row again, now from L2): y = bf16(fp32(fp32(x * inv) * gamma)),
+//     written out if asked, and quantised per 128 columns like quant_1x128
+//     (16 lanes per tile, 8 values per lane).
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ gamma, float eps, int cols,
+                                                            int ld_x, uint16_t* __restrict__ y, int ld_y,
+                                                            uint8_t* __restrict__ q, int ld_q, float* __restrict__ s,
+                                                            int pow2) {
+  __shared__ double red_hi[4], red_lo[4];
+  const long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* xr = x + row * ld_x;
+  double hi = 0.0, lo = 0.0;
+  for (int c = tid * 8; c < cols; c += 256 * 8) {
+    const uint4 p = *reinterpret_cast<const uint4*>(xr + c);
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const double v = (double)__uint_as_float(h ? (w[i] & 0xFFFF0000u) : (w[i] << 16));
+        double t, e;
+        two_sum(hi, v * v, t, e);
+        hi = t;
+        lo += e;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double oh = __shfl_xor(hi, o), ol = __shfl_xor(lo, o);
+    double t, e;
+    two_sum(hi, oh, t, e);
+    hi = t;
+    lo = lo + ol + e;
+  }
+  if (lane == 0) {
+    red_hi[wave] = hi;
+    red_lo[wave] = lo;
+  }
+  __syncthreads();
+  hi = red_hi[0];
+  lo = red_lo[0];
+#pragma unroll
+  for (int w2 = 1; w2 < 4; ++w2) {
+    double t, e;
+    two_sum(hi, red_hi[w2], t, e);
+    hi = t;
+    lo = lo + red_lo[w2] + e;
+  }
+  const double ss = hi + lo;
+  const float inv = (float)(1.0 / sqrt(ss / (double)cols + (double)eps));
+
+  const int sub = tid & 15;
+  const int tpr = cols >> 7;
+  for (int tc = tid >> 4; tc < tpr; tc += 16) {
+    const int c0 = tc * 128 + sub * 8;
+    const uint4 px = *reinterpret_cast<const uint4*>(xr + c0);
+    const uint4 pg = *reinterpret_cast<const uint4*>(gamma + c0);
+    const uint32_t wx[4] = {px.x, px.y, px.z, px.w}, wg[4] = {pg.x, pg.y, pg.z, pg.w};
+    float v[8];
+    uint32_t yb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float xv = __uint_as_float(h ? (wx[i] & 0xFFFF0000u) : (wx[i] << 16));
+        const float gv = __uint_as_float(h ? (wg[i] & 0xFFFF0000u) : (wg[i] << 16));
+        const float t = xv * inv;
+        const uint16_t b = f32_to_bf16_rne(t * gv);
+        v[2 * i + h] = bf16_to_f32(b);
+        pair |= (uint32_t)b << (16 * h);
+      }
+      yb[i] = pair;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = group_max<16>(amax);
+    const float sc = tile_scale(amax, pow2 != 0);
+    uint32_t lo4 = 0, hi4 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo4 |= e4m3_encode(v[i] / sc) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi4 |= e4m3_encode(v[4 + i] / sc) << (8 * i);
+    if (y) *reinterpret_cast<uint4*>(y + row * ld_y + c0) = make_uint4(yb[0], yb[1], yb[2], yb[3]);
+    *reinterpret_cast<uint2*>(q + row * ld_q + c0) = make_uint2(lo4, hi4);
+    if (sub == 0) s[row * tpr + tc] = sc;
+  }
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int rows, int cols, int ld_x,
+                                uint16_t* y, int ld_y, uint8_t* q, int ld_q, float* s, bool pow2, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  rmsnorm_quant_kernel<<<rows, 256, 0, st>>>(x, gamma, eps, cols, ld_x, y, ld_y, q, ld_q, s, pow2);
   return hipGetLastError();
 }
 

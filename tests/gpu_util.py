@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 import synth
-from oracle import ffn, route
+from oracle import ffn, norm, route
 
 DEV = torch.device("cuda:0")
 
@@ -79,19 +79,24 @@ class Layer:
     GEMMs' fragment order), the oracle with its own quant_128x128, from the
     same fp32 values."""
 
-    def __init__(self, shape: synth.MoeShape, device_draw: bool | None = None, bias: np.ndarray | None = None):
+    def __init__(self, shape: synth.MoeShape, device_draw: bool | None = None, bias: np.ndarray | None = None,
+                 ue8m0: bool = False, norm_gamma: np.ndarray | None = None, norm_eps: float = 1e-6):
+        """ue8m0: power-of-two scales everywhere (weights, x, h); norm_gamma: bf16 bits [hidden] of
+        an RMSNorm applied to x first."""
         import sparse_moe_ffn_sigmoid_amd as moe
         self.s = shape
+        self.ue8m0 = ue8m0
+        self.norm = None if norm_gamma is None else (synth.bf16_bits_to_f32(norm_gamma), norm_eps)
         self.device_draw = shape.hidden >= 4096 if device_draw is None else device_draw
-        self.cfg = moe.MoeConfig.of(shape)
+        self.cfg = moe.MoeConfig.of(shape, ue8m0=ue8m0, norm_eps=norm_eps)
         E = shape.n_experts
         self._np_cache: dict[int, tuple[np.ndarray, np.ndarray]] = {}
         self._oracle: dict[int, ffn.QuantExpert] = {}
         w13q, w13s, w2q, w2s = [], [], [], []
         for e in range(E + (1 if shape.n_shared else 0)):
             w13, w2 = self._fp32_dev(e)
-            a, b = moe.quantize_pack_128x128(w13)
-            c, d = moe.quantize_pack_128x128(w2)
+            a, b = moe.quantize_pack_128x128(w13, ue8m0=ue8m0)
+            c, d = moe.quantize_pack_128x128(w2, ue8m0=ue8m0)
             del w13, w2
             w13q.append(a); w13s.append(b); w2q.append(c); w2s.append(d)
         kw = {}
@@ -101,6 +106,8 @@ class Layer:
             del w13q[:E], w13s[:E], w2q[:E], w2s[:E]
         if shape.n_shared:
             kw.update(sh_w13_q=w13q[-1], sh_w13_s=w13s[-1], sh_w2_q=w2q[-1], sh_w2_s=w2s[-1])
+        if norm_gamma is not None:
+            kw["norm_w"] = to_dev(norm_gamma)
         self.wr_bits = synth.gen_router_w(shape) if E else None
         self.bias = bias
         if E:
@@ -128,7 +135,7 @@ class Layer:
         todo = sorted(set(int(i) for i in ids) - set(self._oracle))
         host = {e: self._fp32_host(e) for e in todo}           # device draws happen on this thread
         with ThreadPoolExecutor(16) as ex:
-            res = ex.map(lambda e: (e, ffn.quantize_expert(*host[e])), todo)
+            res = ex.map(lambda e: (e, ffn.quantize_expert(*host[e], ue8m0=self.ue8m0)), todo)
             for e, q in res:
                 self._oracle[e] = q
                 del host[e]
@@ -142,10 +149,53 @@ class Layer:
         s = self.s
         if s.n_experts:
             if scores is None:
-                scores = route.sigmoid_scores(route.router_logits(x_vals, synth.bf16_bits_to_f32(self.wr_bits)))
+                xr = x_vals if self.norm is None else norm.rmsnorm(x_vals, *self.norm)
+                scores = route.sigmoid_scores(route.router_logits(xr, synth.bf16_bits_to_f32(self.wr_bits)))
             idx, _ = route.select(scores, self.bias, s.n_group, s.topk_group, s.top_k, s.routed_scale)
             self.oracle_experts(list(np.unique(idx)) + [s.n_experts] if s.n_shared else list(np.unique(idx)))
         else:
             self.oracle_experts([0])
         return ffn.moe_ffn(x_vals, s.n_experts, s.top_k, s.n_group, s.topk_group, self.expert, scores=scores,
-                           bias=self.bias, n_shared=s.n_shared, routed_scale=s.routed_scale)
+                           bias=self.bias, n_shared=s.n_shared, routed_scale=s.routed_scale, ue8m0=self.ue8m0,
+                           norm=self.norm)
+
+
+def run_layer(layer, xb, scores=None, deterministic=False):
+    """moe_ffn_forward on bf16 bits xb [T, hidden]; returns the output values and the routing."""
+    import sparse_moe_ffn_sigmoid_amd as moe
+    s = layer.s
+    T = xb.shape[0]
+    x = to_dev(xb)
+    if s.n_experts:
+        sc = to_dev(scores) if scores is not None else torch.empty((T, s.n_experts), dtype=torch.float32, device=DEV)
+        ti = torch.empty((T, s.top_k), dtype=torch.int32, device=DEV)
+        tw = torch.empty((T, s.top_k), dtype=torch.float32, device=DEV)
+    else:
+        sc = ti = tw = None
+    out = moe.moe_ffn_forward(x, layer.cfg, layer.weights, scores=sc, scores_given=scores is not None, topk_idx=ti,
+                              topk_w=tw, deterministic=deterministic)
+    torch.cuda.synchronize()
+    r = {"out": bf16_np(out)}
+    if s.n_experts:
+        r.update(scores=sc.cpu().numpy(), topk_idx=ti.cpu().numpy(), topk_w=tw.cpu().numpy())
+    return r
+
+
+def compare_router_run(layer, xb, got, tokens=None):
+    """Router on the device: compare tokens whose expert sets agree; the rest must be near-ties."""
+    s = layer.s
+    xv = synth.bf16_bits_to_f32(xb)
+    tok = np.arange(xb.shape[0]) if tokens is None else np.asarray(tokens)
+    ref = layer.oracle_forward(xv[tok])
+    if not s.n_experts:
+        assert_output(got["out"][tok], ref, f"{s.name} dense")
+        return
+    gi = np.sort(got["topk_idx"][tok], 1)
+    wi = np.sort(ref["topk_idx"], 1)
+    same = (gi == wi).all(1)
+    say(f"  {s.name}: expert sets equal on {same.mean() * 100:.2f}% of {len(tok)} tokens")
+    assert same.mean() >= 0.97
+    b = route.biased(ref["scores"], layer.bias)
+    for i in np.flatnonzero(~same):
+        assert abs(float(b[i, gi[i]].astype(np.float64).sum() - b[i, wi[i]].astype(np.float64).sum())) < 1e-4
+    assert_output(got["out"][tok][same], ref, f"{s.name} (router on device)", rows=same)

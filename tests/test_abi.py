@@ -41,7 +41,7 @@ def test_status_strings(lib):
 
 def _cfg(**kw):
     base = dict(hidden=7168, inter=2048, n_experts=256, top_k=8, n_shared=1, inter_shared=2048, n_group=8,
-                topk_group=4, group_score=0, routed_scale=1.0)
+                topk_group=4, group_score=0, routed_scale=1.0, scale_fmt=0, norm_eps=1e-6)
     base.update(kw)
     return _lib.MoeCfgC(**base)
 
@@ -58,6 +58,9 @@ def test_workspace_sizes(lib):
     assert lib.moe_ffn_workspace_size(64, ctypes.byref(bad)) == 0
     dense = _cfg(n_experts=0, top_k=0, inter=0, inter_shared=18432)
     assert lib.moe_ffn_workspace_size(4096, ctypes.byref(dense)) >= 4096 * 18432
+    assert lib.moe_ffn_workspace_size(64, ctypes.byref(_cfg(scale_fmt=3))) == 0
+    assert lib.moe_ffn_workspace_size(64, ctypes.byref(_cfg(norm_eps=-1.0))) == 0
+    assert lib.moe_ffn_workspace_size(64, ctypes.byref(_cfg(scale_fmt=1))) == n64
     assert lib.moe_permute_workspace_size(4096, 8, 256) == 32 * 256 * 4
     assert lib.moe_permute_workspace_size(10, 8, 2000) == 0
 
@@ -70,15 +73,39 @@ def _err(lib):
 
 
 def test_quant_argument_checks(lib):
-    assert lib.fp8_quant_1x128(FAKE, 1, 4, 100, 100, FAKE, 100, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    F = _lib.MOE_SCALE_F32
+    assert lib.fp8_quant_1x128(FAKE, 1, 4, 100, 100, FAKE, 100, FAKE, F, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
     assert "multiple of 128" in _err(lib)
-    assert lib.fp8_quant_1x128(FAKE, 5, 4, 128, 128, FAKE, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.fp8_quant_1x128(None, 1, 4, 128, 128, FAKE, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.fp8_quant_1x128(FAKE, 1, 4, 128, 64, FAKE, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.fp8_quant_1x128(ctypes.c_void_p(0x10008), 1, 4, 128, 128, FAKE, 128, FAKE, None) == \
+    assert lib.fp8_quant_1x128(FAKE, 5, 4, 128, 128, FAKE, 128, FAKE, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.fp8_quant_1x128(None, 1, 4, 128, 128, FAKE, 128, FAKE, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.fp8_quant_1x128(FAKE, 1, 4, 128, 64, FAKE, 128, FAKE, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.fp8_quant_1x128(ctypes.c_void_p(0x10008), 1, 4, 128, 128, FAKE, 128, FAKE, F, None) == \
         _lib.MOE_ERR_INVALID_ARG
-    assert lib.fp8_quant_1x128(None, 1, 0, 128, 128, None, 128, None, None) == _lib.MOE_OK   # empty: no-op
-    assert lib.fp8_quant_128x128(FAKE, 130, 128, FAKE, FAKE, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert lib.fp8_quant_1x128(FAKE, 1, 4, 128, 128, FAKE, 128, FAKE, 2, None) == _lib.MOE_ERR_INVALID_ARG  # format
+    assert lib.fp8_quant_1x128(None, 1, 0, 128, 128, None, 128, None, F, None) == _lib.MOE_OK   # empty: no-op
+    assert lib.fp8_quant_128x128(FAKE, 130, 128, FAKE, FAKE, F, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert lib.fp8_quant_128x128(FAKE, 128, 128, FAKE, FAKE, -1, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_rmsnorm_quant_argument_checks(lib):
+    F, U = _lib.MOE_SCALE_F32, _lib.MOE_SCALE_UE8M0
+    f = lib.fp8_rmsnorm_quant_1x128
+    assert f(FAKE, FAKE, 1e-6, 4, 200, 200, None, 0, FAKE, 200, FAKE, F, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, -1.0, 4, 256, 256, None, 0, FAKE, 256, FAKE, F, None) == _lib.MOE_ERR_INVALID_ARG   # eps < 0
+    assert f(FAKE, FAKE, float("nan"), 4, 256, 256, None, 0, FAKE, 256, FAKE, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(FAKE, None, 1e-6, 4, 256, 256, None, 0, FAKE, 256, FAKE, U, None) == _lib.MOE_ERR_INVALID_ARG  # gamma
+    assert f(FAKE, FAKE, 1e-6, 4, 256, 256, FAKE, 128, FAKE, 256, FAKE, F, None) == _lib.MOE_ERR_INVALID_ARG  # ld_y
+    assert f(FAKE, FAKE, 1e-6, 4, 256, 256, None, 0, FAKE, 256, FAKE, 7, None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(None, None, 1e-6, 0, 256, 256, None, 0, None, 256, None, F, None) == _lib.MOE_OK               # empty
+
+
+def test_bias_update_argument_checks(lib):
+    f = lib.moe_bias_update
+    assert f(FAKE, 4, 8, 2000, 0.01, FAKE, None, None) == _lib.MOE_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, 4, 0, 16, 0.01, FAKE, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 16, float("inf"), FAKE, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 8, 16, 0.01, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert f(None, 4, 8, 16, 0.01, FAKE, None, None) == _lib.MOE_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -129,6 +156,9 @@ def test_gemm_checks(lib):
         _lib.MOE_ERR_UNSUPPORTED_SHAPE
     assert lib.fp8_grouped_gemm_blockscaled(*args, 4, 64, 256, 128, 9, ctypes.byref(epi), FAKE, None) == \
         _lib.MOE_ERR_INVALID_ARG
+    bad = _lib.MoeEpiC(FAKE.value, None, None, 5)
+    assert lib.fp8_grouped_gemm_blockscaled(*args, 4, 64, 256, 128, 2, ctypes.byref(bad), FAKE, None) == \
+        _lib.MOE_ERR_INVALID_ARG                                    # unknown scale format
 
 
 def test_forward_checks(lib):
@@ -151,3 +181,6 @@ def test_forward_checks(lib):
                                0, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_ffn_forward(None, 0, ctypes.byref(c), ctypes.byref(w), None, 0, None, None, None, None, 0, None) == \
         _lib.MOE_OK
+    wn = _lib.MoeWeightsC(*([0x10000] * 10 + [0x10008]))                                    # norm_w misaligned
+    assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(c), ctypes.byref(wn), FAKE, need, FAKE, None, None, None, 0,
+                               None) == _lib.MOE_ERR_INVALID_ARG

@@ -21,51 +21,14 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import sparse_moe_ffn_sigmoid_amd as moe
     from gpu_util import DEV, Layer, assert_output, bf16_np, say, to_dev
+    from gpu_util import compare_router_run as _compare_router_run
+    from gpu_util import run_layer as _run
 
 MID_A = synth.MoeShape("mid_a", 10, 200, 512, 256, 32, 4, 1, 256, 4, 2)
 MID_B = synth.MoeShape("mid_b", 11, 1024, 384, 256, 16, 4, 1, 384, 4, 4)
 MID_ATOMIC = synth.MoeShape("mid_atomic", 12, 2304, 256, 128, 16, 4, 1, 128, 4, 2)
 NO_SHARED = synth.MoeShape("no_shared", 13, 100, 256, 128, 16, 2, 0, 0, 4, 2)
 DENSE_SMALL = synth.MoeShape("dense_small", 14, 300, 512, 0, 0, 0, 1, 640, 1, 1)
-
-
-def _run(layer, xb, scores=None, deterministic=False):
-    s = layer.s
-    T = xb.shape[0]
-    x = to_dev(xb)
-    if s.n_experts:
-        sc = to_dev(scores) if scores is not None else torch.empty((T, s.n_experts), dtype=torch.float32, device=DEV)
-        ti = torch.empty((T, s.top_k), dtype=torch.int32, device=DEV)
-        tw = torch.empty((T, s.top_k), dtype=torch.float32, device=DEV)
-    else:
-        sc = ti = tw = None
-    out = moe.moe_ffn_forward(x, layer.cfg, layer.weights, scores=sc, scores_given=scores is not None, topk_idx=ti,
-                              topk_w=tw, deterministic=deterministic)
-    torch.cuda.synchronize()
-    r = {"out": bf16_np(out)}
-    if s.n_experts:
-        r.update(scores=sc.cpu().numpy(), topk_idx=ti.cpu().numpy(), topk_w=tw.cpu().numpy())
-    return r
-
-
-def _compare_router_run(layer, xb, got, tokens=None):
-    """Router on the device: compare tokens whose expert sets agree; the rest must be near-ties."""
-    s = layer.s
-    xv = synth.bf16_bits_to_f32(xb)
-    tok = np.arange(xb.shape[0]) if tokens is None else np.asarray(tokens)
-    ref = layer.oracle_forward(xv[tok])
-    if not s.n_experts:
-        assert_output(got["out"][tok], ref, f"{s.name} dense")
-        return
-    gi = np.sort(got["topk_idx"][tok], 1)
-    wi = np.sort(ref["topk_idx"], 1)
-    same = (gi == wi).all(1)
-    say(f"  {s.name}: expert sets equal on {same.mean() * 100:.2f}% of {len(tok)} tokens")
-    assert same.mean() >= 0.97
-    b = route.biased(ref["scores"], layer.bias)
-    for i in np.flatnonzero(~same):
-        assert abs(float(b[i, gi[i]].astype(np.float64).sum() - b[i, wi[i]].astype(np.float64).sum())) < 1e-4
-    assert_output(got["out"][tok][same], ref, f"{s.name} (router on device)", rows=same)
 
 
 @pytest.fixture(scope="module")
