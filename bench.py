@@ -74,9 +74,10 @@ class HipEvents:
         self.rt.hipEventDestroy(e)
 
 
-def build_layer(shape, dev):
-    """Device weights of the layer: fp32 draws quantised by fp8_quant_128x128, then packed into the
-    GEMMs' fragment order (moe_pack_weights), expert by expert."""
+def build_layer(shape, dev, ue8m0: bool = False, rmsnorm: bool = False):
+    """Device weights of the layer: fp32 draws quantised by fp8_quant_128x128 (power-of-two scales with
+    ue8m0), then packed into the GEMMs' fragment order (moe_pack_weights), expert by expert; with rmsnorm
+    an RMSNorm weight (bf16, seeded uniform in [0.5, 1.5]) goes in front."""
     import torch
 
     import sparse_moe_ffn_sigmoid_amd as moe
@@ -90,17 +91,21 @@ def build_layer(shape, dev):
         kw["w2_q"] = torch.empty((E, d, W), dtype=torch.uint8, device=dev)
         kw["w2_s"] = torch.empty((E, d // 128, W // 128), dtype=torch.float32, device=dev)
         for e in range(E):
-            moe.quantize_pack_128x128(synth.torch_expert_weight(shape, e, "w13", dev), q=kw["w13_q"][e], s=kw["w13_s"][e])
-            moe.quantize_pack_128x128(synth.torch_expert_weight(shape, e, "w2", dev), q=kw["w2_q"][e], s=kw["w2_s"][e])
+            moe.quantize_pack_128x128(synth.torch_expert_weight(shape, e, "w13", dev), q=kw["w13_q"][e], s=kw["w13_s"][e],
+                                      ue8m0=ue8m0)
+            moe.quantize_pack_128x128(synth.torch_expert_weight(shape, e, "w2", dev), q=kw["w2_q"][e], s=kw["w2_s"][e],
+                                      ue8m0=ue8m0)
         wr = synth.gen_router_w(shape)
         import numpy as np
         kw["w_router"] = torch.from_numpy(wr.view(np.int16)).to(dev).view(torch.bfloat16)
         if shape.skewed:
             kw["bias"] = torch.from_numpy(synth.skew_bias()).to(dev)
     if shape.n_shared:
-        a, b = moe.quantize_pack_128x128(synth.torch_expert_weight(shape, E, "w13", dev))
-        c, e_ = moe.quantize_pack_128x128(synth.torch_expert_weight(shape, E, "w2", dev))
+        a, b = moe.quantize_pack_128x128(synth.torch_expert_weight(shape, E, "w13", dev), ue8m0=ue8m0)
+        c, e_ = moe.quantize_pack_128x128(synth.torch_expert_weight(shape, E, "w2", dev), ue8m0=ue8m0)
         kw.update(sh_w13_q=a, sh_w13_s=b, sh_w2_q=c, sh_w2_s=e_)
+    if rmsnorm:
+        kw["norm_w"] = norm_weight(shape, dev)
     torch.cuda.synchronize()
     return moe.MoeWeights(**kw)
 
@@ -223,6 +228,61 @@ def traffic_summary(d: str, shape) -> None:
     print(f"wrote {traffic_file(shape)}: {traffic / 1e9:.3f} GB per launch")
 
 
+def norm_weight(shape, dev):
+    import numpy as np
+    import torch
+
+    import synth
+    g = np.random.default_rng(shape.cfg_id).uniform(0.5, 1.5, shape.hidden).astype(np.float32)
+    return torch.from_numpy(synth.f32_to_bf16_bits(g).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def time_launches(hip, stream, fn, n: int = 20) -> float:
+    """Average ms of fn() (which enqueues on `stream`) over n launches, HIP events on that stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = hip.create(), hip.create()
+    hip.record(a, stream)
+    for _ in range(n):
+        fn()
+    hip.record(b, stream)
+    hip.sync(b)
+    ms = hip.ms(a, b) / n
+    hip.destroy(a)
+    hip.destroy(b)
+    return ms
+
+
+def next_rows(shape, x, idx, hip, stream, dev) -> dict:
+    """Per-launch timing of the kernels next to the layer, on this workload's tensors: the RMSNorm
+    fused with the 1x128 quantisation (x [T, hidden] -> normalised bf16 rows + codes + scales) and
+    the routing-bias balancing step on this step's expert choices."""
+    import torch
+
+    from sparse_moe_ffn_sigmoid_amd import _lib
+    lib = _lib.load()
+    T, d = x.shape
+    g = norm_weight(shape, dev)
+    y = torch.empty_like(x)
+    q = torch.empty((T, d), dtype=torch.uint8, device=dev)
+    s = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
+    args = [ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(g.data_ptr()), 1e-6, T, d, d, ctypes.c_void_p(y.data_ptr()),
+            d, ctypes.c_void_p(q.data_ptr()), d, ctypes.c_void_p(s.data_ptr()), 0, stream]
+    ms = time_launches(hip, stream, lambda: lib.fp8_rmsnorm_quant_1x128(*args))
+    nbytes = T * d * (2 + 2 + 1) + T * (d // 128) * 4 + 2 * d
+    res = {"rmsnorm_quant_1x128": {"us": ms * 1e3, "hbm_gbs_algorithmic": nbytes / ms / 1e6,
+                                   "pct_hbm_peak": 100 * nbytes / ms / 1e6 / HBM_PEAK_GBS, "bytes": nbytes}}
+    if shape.n_experts:
+        bias = torch.zeros(shape.n_experts, dtype=torch.float32, device=dev)
+        k = idx.shape[1]
+        bargs = [ctypes.c_void_p(idx.data_ptr()), T, k, shape.n_experts, 1e-3, ctypes.c_void_p(bias.data_ptr()), None,
+                 stream]
+        ms = time_launches(hip, stream, lambda: lib.moe_bias_update(*bargs))
+        res["bias_update"] = {"us": ms * 1e3, "assignments": T * k}
+    return res
+
+
 def algorithmic_bytes(shape, touched: int) -> dict:
     """Bytes the method must move (codes + scales of experts with load > 0 and the shared
     expert, router weights and bias, x in and the output, both bf16)."""
@@ -284,6 +344,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--ue8m0", action="store_true", help="power-of-two (UE8M0) scales for weights and activations")
+    ap.add_argument("--rmsnorm", action="store_true", help="the RMSNorm in front, fused with x's quantisation")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB")
     ap.add_argument("--traffic-summary", metavar="DIR")
     args = ap.parse_args()
@@ -310,8 +372,8 @@ def main():
     dev = torch.device("cuda:0")
     print(f"[bench] {shape.name}: building weights on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     t_build = time.perf_counter()
-    weights = build_layer(shape, dev)
-    cfg = moe.MoeConfig.of(shape)
+    weights = build_layer(shape, dev, ue8m0=args.ue8m0, rmsnorm=args.rmsnorm)
+    cfg = moe.MoeConfig.of(shape, ue8m0=args.ue8m0)
     x_bits = synth.gen_x(shape)
     x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     T = shape.tokens
@@ -375,7 +437,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": gate_up_flops / t_gu / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(shape)
+    roof["traffic"] = stored_traffic(shape) if not (args.ue8m0 or args.rmsnorm) else None   # counted on the default
     roof["kernel"] = gate_up_kernel(shape) + " (gate/up GEMM, SwiGLU + requantisation epilogue)"
     roof["avg_ms"] = stage["gate_up_gemm"]
     attainable = max(flops / (FP8_PEAK_TFLOPS * 1e12), nbytes["layer"] / (HBM_PEAK_GBS * 1e9))
@@ -387,6 +449,7 @@ def main():
         "config": {"workload": shape.name, "tokens": T, "hidden": shape.hidden, "inter": shape.inter,
                    "n_experts": shape.n_experts, "top_k": shape.top_k, "n_shared": shape.n_shared,
                    "inter_shared": shape.inter_shared, "n_group": shape.n_group, "topk_group": shape.topk_group,
+                   "scales": "ue8m0" if args.ue8m0 else "fp32", "rmsnorm": bool(args.rmsnorm),
                    "parallelism": "single GPU"},
         "fp8_tflops": tflops, "pct_fp8_mfma_peak": 100 * tflops / FP8_PEAK_TFLOPS,
         "hbm_gbs_algorithmic": hbm_gbs, "pct_hbm_peak": 100 * hbm_gbs / HBM_PEAK_GBS,
@@ -394,6 +457,7 @@ def main():
         "experts_touched": touched,
         "load_max_over_mean": float(loads.max() / loads.mean()) if loads.size else None,
         "roofline": roof,
+        "next_rows": next_rows(shape, x, idx, hip, stream, dev),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)

@@ -148,27 +148,33 @@ hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, 
 
 // RMSNorm fused with the 1x128 quantisation (llm-architectures-explained,
 // "DeepSeek-R1", facts rows "Norm placement" / "Norm type": RMSNorm right before
-// the MLP).  One workgroup per row:
-//   pass 1: the sum of squares.  Squares of bf16 values are exact in fp64; they
-//     are accumulated in double-double (TwoSum) per lane and reduced pairwise,
-//     then rounded once, which gives the exactly rounded fp64 sum for any
-//     realistic row (so the result does not depend on the summation order);
+// the MLP).  One workgroup (16 groups of 16 lanes) per row; group g handles the
+// 128-column tiles g, g + 16, ...; each lane 8 consecutive values of a tile.
+//   the sum of squares: squares of bf16 values are exact in fp64; they are
+//     accumulated in double-double (TwoSum) per lane and reduced pairwise, then
+//     rounded once, which gives the exactly rounded fp64 sum for any realistic
+//     row (so the result does not depend on the summation order);
 //   inv = fp32(1 / sqrt(sum / cols + eps)) in fp64;
-//   pass 2 (the row again, now from L2): y = bf16(fp32(fp32(x * inv) * gamma)),
-//     written out if asked, and quantised per 128 columns like quant_1x128
-//     (16 lanes per tile, 8 values per lane).
+//   y = bf16(fp32(fp32(x * inv) * gamma)), written out if asked, and quantised
+//     per 128 columns like quant_1x128.
+// NT > 0: the row stays in registers between the two steps (NT tiles per group,
+// cols <= 16 * NT * 128), one read of x; NT == 0: any width, the second step
+// reads the row again (from L2).
+template <int NT>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ gamma, float eps, int cols,
                                                             int ld_x, uint16_t* __restrict__ y, int ld_y,
                                                             uint8_t* __restrict__ q, int ld_q, float* __restrict__ s,
                                                             int pow2) {
+  constexpr int R = NT > 0 ? NT : 1;
   __shared__ double red_hi[4], red_lo[4];
   const long row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = tid >> 4, sub = tid & 15;
+  const int tpr = cols >> 7;
   const uint16_t* xr = x + row * ld_x;
+  uint4 keep[R];
   double hi = 0.0, lo = 0.0;
-  for (int c = tid * 8; c < cols; c += 256 * 8) {
-    const uint4 p = *reinterpret_cast<const uint4*>(xr + c);
+  auto accumulate = [&](const uint4 p) {
     const uint32_t w[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -181,6 +187,16 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
         lo += e;
       }
     }
+  };
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int tc = grp + 16 * i;
+      keep[i] = tc < tpr ? *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
+      accumulate(keep[i]);                       // zeros add nothing
+    }
+  } else {
+    for (int tc = grp; tc < tpr; tc += 16) accumulate(*reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -207,11 +223,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
   const double ss = hi + lo;
   const float inv = (float)(1.0 / sqrt(ss / (double)cols + (double)eps));
 
-  const int sub = tid & 15;
-  const int tpr = cols >> 7;
-  for (int tc = tid >> 4; tc < tpr; tc += 16) {
+  auto emit = [&](int tc, const uint4 px) {
     const int c0 = tc * 128 + sub * 8;
-    const uint4 px = *reinterpret_cast<const uint4*>(xr + c0);
     const uint4 pg = *reinterpret_cast<const uint4*>(gamma + c0);
     const uint32_t wx[4] = {px.x, px.y, px.z, px.w}, wg[4] = {pg.x, pg.y, pg.z, pg.w};
     float v[8];
@@ -243,13 +256,23 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     if (y) *reinterpret_cast<uint4*>(y + row * ld_y + c0) = make_uint4(yb[0], yb[1], yb[2], yb[3]);
     *reinterpret_cast<uint2*>(q + row * ld_q + c0) = make_uint2(lo4, hi4);
     if (sub == 0) s[row * tpr + tc] = sc;
+  };
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (grp + 16 * i < tpr) emit(grp + 16 * i, keep[i]);     // uniform within each 16-lane group
+  } else {
+    for (int tc = grp; tc < tpr; tc += 16) emit(tc, *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8));
   }
 }
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int rows, int cols, int ld_x,
                                 uint16_t* y, int ld_y, uint8_t* q, int ld_q, float* s, bool pow2, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  rmsnorm_quant_kernel<<<rows, 256, 0, st>>>(x, gamma, eps, cols, ld_x, y, ld_y, q, ld_q, s, pow2);
+  if (cols <= 16 * 4 * 128)
+    rmsnorm_quant_kernel<4><<<rows, 256, 0, st>>>(x, gamma, eps, cols, ld_x, y, ld_y, q, ld_q, s, pow2);
+  else
+    rmsnorm_quant_kernel<0><<<rows, 256, 0, st>>>(x, gamma, eps, cols, ld_x, y, ld_y, q, ld_q, s, pow2);
   return hipGetLastError();
 }
 

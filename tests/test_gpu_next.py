@@ -63,7 +63,8 @@ def _norm_case(T, d, seed, scale=1.0):
 
 
 @pytest.mark.parametrize("ue8m0", [False, True])
-@pytest.mark.parametrize("T,d,scale", [(1, 128, 1.0), (37, 7168, 1.0), (64, 256, 3e-3), (300, 1024, 40.0)])
+@pytest.mark.parametrize("T,d,scale", [(1, 128, 1.0), (37, 7168, 1.0), (64, 256, 3e-3), (300, 1024, 40.0),
+                                       (9, 8320, 1.0)])
 def test_rmsnorm_quant_bit_exact(T, d, scale, ue8m0):
     say(f"rmsnorm+quant T={T} d={d} scale={scale} ue8m0={ue8m0}")
     xb, xv = _norm_case(T, d, T * 31 + d, scale)
