@@ -69,7 +69,8 @@ extern "C" {
 
 /* ---- flags ---- */
 #define MOE_ROUTE_SCORES_GIVEN 1       /* moe_route / moe_ffn_forward: `scores` is an input   */
-#define MOE_FWD_DETERMINISTIC 2        /* moe_ffn_forward: slot-ordered combine, no atomics   */
+#define MOE_FWD_DETERMINISTIC 2        /* moe_ffn_forward: slot-ordered combine (always the case;
+                                          accepted for callers that ask for it explicitly)      */
 
 /* ---- grouped GEMM epilogues ---- */
 #define MOE_EPI_STORE_F32 0            /* out f32 [M][N]                                        */
@@ -249,8 +250,8 @@ MOE_API size_t moe_ffn_workspace_size(int T, const moe_cfg_t* cfg);
  *   x bf16 [T][hidden]; out bf16 [T][hidden];
  *   scores f32 [T][E], topk_idx i32 [T][k], topk_w f32 [T][k]: optional outputs
  *   (NULL to skip); with MOE_ROUTE_SCORES_GIVEN `scores` is an input instead.
- *   MOE_FWD_DETERMINISTIC: bit-reproducible combine (slot-ordered) instead of
- *   fp32 atomics; it is also what the library does when T is small.
+ *   The combine is slot-ordered in fp32, so the output is bit-reproducible run to
+ *   run (MOE_FWD_DETERMINISTIC is accepted and changes nothing).
  * ws: at least moe_ffn_workspace_size(T, cfg) bytes, 256-byte aligned.     */
 MOE_API int moe_ffn_forward(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
                     size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w, int flags,

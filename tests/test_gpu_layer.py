@@ -26,7 +26,7 @@ if torch.cuda.is_available():
 
 MID_A = synth.MoeShape("mid_a", 10, 200, 512, 256, 32, 4, 1, 256, 4, 2)
 MID_B = synth.MoeShape("mid_b", 11, 1024, 384, 256, 16, 4, 1, 384, 4, 4)
-MID_ATOMIC = synth.MoeShape("mid_atomic", 12, 2304, 256, 128, 16, 4, 1, 128, 4, 2)
+MID_LARGE = synth.MoeShape("mid_large", 12, 2304, 256, 128, 16, 4, 1, 128, 4, 2)   # 9216 assignments
 NO_SHARED = synth.MoeShape("no_shared", 13, 100, 256, 128, 16, 2, 0, 0, 4, 2)
 DENSE_SMALL = synth.MoeShape("dense_small", 14, 300, 512, 0, 0, 0, 1, 640, 1, 1)
 
@@ -62,7 +62,16 @@ def test_tiny_deterministic_repeat(tiny):
     assert np.array_equal(a["out"], b["out"])
 
 
-@pytest.mark.parametrize("shape", [MID_A, MID_B, MID_ATOMIC, NO_SHARED, DENSE_SMALL])
+def test_large_batch_is_bit_reproducible():
+    """The combine is slot-ordered at every batch size: repeated runs agree bit for bit."""
+    say("forward mid_large twice: bit-reproducible")
+    layer = Layer(MID_LARGE)
+    xb = synth.gen_x(MID_LARGE)
+    a, b = _run(layer, xb), _run(layer, xb)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["topk_idx"], b["topk_idx"])
+
+
+@pytest.mark.parametrize("shape", [MID_A, MID_B, MID_LARGE, NO_SHARED, DENSE_SMALL])
 def test_mid_shapes(shape):
     say(f"forward {shape.name} T={shape.tokens} d={shape.hidden} E={shape.n_experts} k={shape.top_k}")
     layer = Layer(shape)
