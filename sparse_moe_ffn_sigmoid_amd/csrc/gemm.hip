@@ -467,18 +467,26 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   const float* const bs = (si ? s1.b_s : s0.b_s) + (long long)g * (si ? s1.bs_stride : s0.bs_stride);
 
   // ---- per-lane global sources of this wave's loads (advanced by kb each K block) ----
-  // A: wave load i covers 16-row block ab = (wave * A_LOADS + i) / 2, half h = i % 2;
-  //    lane (r16, q) loads row 16 ab + r16, bytes 64 h + 16 q: LDS slot = lane (fragment order).
+  // A: wave load i covers tile rows 8 li .. 8 li + 7 (li = wave * A_LOADS + i) as whole
+  //    128-byte rows (full cache lines): lane l takes row r = 8 li + l / 8 and fills slot l % 8 of
+  //    that row in LDS with the row's 16-byte chunk (l % 8) ^ (r % 8).  The XOR spreads a fragment
+  //    read (16 rows x one chunk) over the LDS banks (measured conflict-free on gfx950, where a
+  //    plain row-major layout conflicts 4-way and an XOR with (r % 8) ^ (r / 8 % 2) 2-way).
   const uint8_t* a_src[A_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     const int li = wave * A_LOADS + i;
-    const int ab = li >> 1, h = li & 1;
-    int m = m0 + ab * 16 + r16;
+    const int r = 8 * li + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    int m = m0 + r;
     m = m < m_end ? m : m0;
     const long src = gat ? (long)gat[m] : (long)m;
-    a_src[i] = a_q + src * K + 64 * h + 16 * q;
+    a_src[i] = a_q + src * K + 16 * c;
   }
+  // where this lane's A fragment pieces sit inside a 16-row block (2 KB): row r16, chunks q and 4 + q
+  const int a_swz = r16 & 7;
+  const int a_off_lo = r16 * 128 + 16 * (q ^ a_swz);
+  const int a_off_hi = r16 * 128 + 16 * ((4 + q) ^ a_swz);
   // B: wave load i covers local block bb = (wave * B_LOADS + i) / 2, half h = i % 2.
   const uint8_t* b_src[B_LOADS];
 #pragma unroll
@@ -532,10 +540,11 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 
   // MFMAs and scale promotion of one K block from the LDS stage at st (+ this lane's offset)
   auto compute = [&](const uint8_t* st) {
+    const uint8_t* const stb = st - lane_off;
     auto load_a = [&](int mi) {
       const int ab = wm * MT + mi;
-      const v4i lo = *reinterpret_cast<const v4i*>(st + ab * 2048);
-      const v4i hi = *reinterpret_cast<const v4i*>(st + ab * 2048 + 1024);
+      const v4i lo = *reinterpret_cast<const v4i*>(stb + ab * 2048 + a_off_lo);
+      const v4i hi = *reinterpret_cast<const v4i*>(stb + ab * 2048 + a_off_hi);
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     // LDS reads in the order the MFMAs need them: the first A fragment, then the B fragments;
