@@ -731,9 +731,10 @@ static void launch_mfma_cfg(const GemmArgs& args, dim3 grid, hipStream_t st) {
   mfma_gemm_kernel<WM, WN, MT, EPI><<<grid, 64 * WM * WN, 0, st>>>(args);
 }
 
-// bm = rows per tile: 32, 64 or 128.  The gate/up GEMM (exact bf16 path, VALU-heavier)
-// runs 8 waves with 64x64 wave tiles (two waves per SIMD co-issue VALU and MFMA);
-// the FP8 GEMMs run 4 waves with 64x128 wave tiles (half the LDS reads per MFMA).
+// bm = rows per tile: 32, 64 or 128.  Tiles of 64 or more rows run 8 waves with 64-column
+// wave tiles (two waves per SIMD: one's LDS reads and VALU work overlap the other's MFMAs;
+// measured 5-15% faster for the FP8 down GEMM than 4 waves with 128-column wave tiles, which
+// need half the LDS reads per MFMA); 32-row tiles run 4 waves.
 template <int MT>
 static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
   const bool swiglu = epi == kEpiSwiglu;
@@ -749,8 +750,14 @@ static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
       if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiSwiglu>(args, grid, st);
       else launch_mfma_cfg<2, 2, MT, kEpiSwiglu>(args, grid, st);
       break;
-    case kEpiF32: launch_mfma_cfg<2, 2, MT, kEpiF32>(args, grid, st); break;
-    case kEpiBf16: launch_mfma_cfg<2, 2, MT, kEpiBf16>(args, grid, st); break;
+    case kEpiF32:
+      if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiF32>(args, grid, st);
+      else launch_mfma_cfg<2, 2, MT, kEpiF32>(args, grid, st);
+      break;
+    case kEpiBf16:
+      if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiBf16>(args, grid, st);
+      else launch_mfma_cfg<2, 2, MT, kEpiBf16>(args, grid, st);
+      break;
     default: launch_mfma_cfg<2, 2, MT, kEpiScatter>(args, grid, st); break;
   }
   return hipGetLastError();
