@@ -9,83 +9,79 @@
 namespace moefp8 {
 
 // scores[t][e] = sigmoid(sum_d x[t][d] * w[e][d]); bf16 operands on the gfx950
-// 16x16x32 bf16 MFMA, fp32 accumulation.  A workgroup is 4 waves over 64
-// tokens (16 per wave) and shares one slice of 16*NT experts; operands are read
-// straight from global memory (the slice of router weights stays in L2).
-template <int NT>
-__global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                     int T, int E, int D, float* __restrict__ scores) {
+// 16x16x32 bf16 MFMA, fp32 accumulation.  A workgroup covers 16*MTK tokens x
+// 16*NT experts; its NW waves split the hidden dimension (in 32-wide steps) and
+// add their partial logits through LDS in a fixed order (deterministic).  Each
+// wave issues the loads of U steps before their MFMAs, straight from global
+// memory (the router weights stay in L2).  Small batches use many waves per
+// workgroup (the 3.7 MB of router weights spread over many CUs); large ones a
+// 64 x 64 tile, so each token row is read once per 64 experts and each router
+// weight row once per 64 tokens.
+template <int NW, int NT, int MTK, int U>
+__global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ w, int T, int E, int D,
+                                                                float* __restrict__ scores) {
+  __shared__ v4f part[NW][MTK * NT][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, q = lane >> 4;
-  const int t0 = blockIdx.x * 64 + wave * 16;
-  const int e0 = blockIdx.y * 16 * NT;
-  const int ta = min(t0 + r16, T - 1);
-  const uint16_t* xa = x + (long)ta * D + 8 * q;
+  const int t0 = blockIdx.x * 16 * MTK, e0 = blockIdx.y * 16 * NT;
+  const int steps = D >> 5;                     // 32-wide K steps, split as evenly as possible
+  const int s0 = (steps * wave) / NW, s1 = (steps * (wave + 1)) / NW;
+  const uint16_t* xa[MTK];
+#pragma unroll
+  for (int i = 0; i < MTK; ++i) xa[i] = x + (long)min(t0 + 16 * i + r16, T - 1) * D + 8 * q;
   const uint16_t* wb[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) wb[j] = w + (long)(e0 + 16 * j + r16) * D + 8 * q;
-  v4f acc[NT];
+  v4f acc[MTK][NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < D; k += 32) {
-    const v8bf a = *reinterpret_cast<const v8bf*>(xa + k);
+  for (int i = 0; i < MTK; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const v8bf b = *reinterpret_cast<const v8bf*>(wb[j] + k);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
-    }
-  }
-  // lane holds rows (tokens) 4q..4q+3 of the wave's 16, column (expert) r16
+    for (int j = 0; j < NT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  int k = s0;
+  for (; k + U <= s1; k += U) {
+    v8bf a[MTK][U], b[NT][U];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * q + i;
-      if (t < T) scores[(long)t * E + e0 + 16 * j + r16] = 1.0f / (1.0f + expf(-acc[j][i]));
-    }
-  }
-}
-
-// Small batches: one workgroup per 16 tokens x 16 experts, its 4 waves split
-// the hidden dimension in quarters (8 MFMA steps in flight per wave) and add
-// their partial logits through LDS; enough workgroups to spread the 3.7 MB of
-// router weights over many CUs even at T = 64.
-__global__ __launch_bounds__(256) void router_splitk_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w, int T, int E, int D,
-                                                            float* __restrict__ scores) {
-  __shared__ v4f part[4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r16 = lane & 15, q = lane >> 4;
-  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
-  const int ta = min(t0 + r16, T - 1);
-  const int kq = D >> 2;                        // D % 128 == 0: quarters are multiples of 32
-  const uint16_t* xa = x + (long)ta * D + wave * kq + 8 * q;
-  const uint16_t* wb = w + (long)(e0 + r16) * D + wave * kq + 8 * q;
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  int k = 0;
-  for (; k + 256 <= kq; k += 256) {
-    v8bf a[8], b[8];
+      for (int i = 0; i < MTK; ++i) a[i][u] = *reinterpret_cast<const v8bf*>(xa[i] + 32 * (k + u));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      a[u] = *reinterpret_cast<const v8bf*>(xa + k + 32 * u);
-      b[u] = *reinterpret_cast<const v8bf*>(wb + k + 32 * u);
+      for (int j = 0; j < NT; ++j) b[j][u] = *reinterpret_cast<const v8bf*>(wb[j] + 32 * (k + u));
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < MTK; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][u], b[j][u], acc[i][j], 0, 0, 0);
   }
-  for (; k < kq; k += 32) {
-    const v8bf a = *reinterpret_cast<const v8bf*>(xa + k);
-    const v8bf b = *reinterpret_cast<const v8bf*>(wb + k);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  for (; k < s1; ++k) {
+#pragma unroll
+    for (int i = 0; i < MTK; ++i) {
+      const v8bf a = *reinterpret_cast<const v8bf*>(xa[i] + 32 * k);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, *reinterpret_cast<const v8bf*>(wb[j] + 32 * k),
+                                                            acc[i][j], 0, 0, 0);
+    }
   }
-  part[wave][lane] = acc;
+#pragma unroll
+  for (int i = 0; i < MTK; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) part[wave][i * NT + j][lane] = acc[i][j];
   __syncthreads();
-  if (wave == 0) {
-    const v4f t = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  // tile (i, j) is finished by wave (i * NT + j) % NW: fixed-order sum over the waves, then the sigmoid
+  for (int tile = wave; tile < MTK * NT; tile += NW) {
+    v4f t = part[0][tile][lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = t0 + 4 * q + i;
-      if (tt < T) scores[(long)tt * E + e0 + r16] = 1.0f / (1.0f + expf(-t[i]));
+    for (int w2 = 1; w2 < NW; ++w2) t += part[w2][tile][lane];
+    const int i = tile / NT, j = tile % NT;
+    // lane holds rows (tokens) 4q..4q+3 of token tile i, column (expert) r16 of expert tile j
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = t0 + 16 * i + 4 * q + r;
+      if (tt < T) scores[(long)tt * E + e0 + 16 * j + r16] = 1.0f / (1.0f + expf(-t[r]));
     }
   }
 }
@@ -245,14 +241,12 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const unsigned gx = (unsigned)((T + 63) / 64);
-  if (T <= 512) {
-    router_splitk_kernel<<<dim3((T + 15) / 16, E / 16), 256, 0, st>>>(x, w, T, E, D, scores);
-  } else if (E % 64 == 0) {
-    router_kernel<4><<<dim3(gx, E / 64), 256, 0, st>>>(x, w, T, E, D, scores);
-  } else {
-    router_kernel<1><<<dim3(gx, E / 16), 256, 0, st>>>(x, w, T, E, D, scores);
-  }
+  if (T <= 512)
+    router_splitk_kernel<16, 1, 1, 8><<<dim3((T + 15) / 16, E / 16), 1024, 0, st>>>(x, w, T, E, D, scores);
+  else if (E % 64 == 0)
+    router_splitk_kernel<4, 4, 4, 4><<<dim3((T + 63) / 64, E / 64), 256, 0, st>>>(x, w, T, E, D, scores);
+  else
+    router_splitk_kernel<4, 1, 4, 4><<<dim3((T + 63) / 64, E / 16), 256, 0, st>>>(x, w, T, E, D, scores);
   return hipGetLastError();
 }
 
