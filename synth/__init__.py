@@ -76,7 +76,11 @@ V3_DECODE = MoeShape("v3_decode", 1, 64, 7168, 2048, 256, 8, 1, 2048, 8, 4)
 DENSE_FFN = MoeShape("dense_ffn", 2, 4096, 7168, 0, 0, 0, 1, 18432, 1, 1)
 V3_PREFILL = MoeShape("v3_prefill", 3, 4096, 7168, 2048, 256, 8, 1, 2048, 8, 4)
 V3_SKEW = MoeShape("v3_skew", 4, 16384, 7168, 2048, 256, 8, 1, 2048, 8, 4, skewed=True)
-SHAPES = {s.name: s for s in (TINY, V3_DECODE, DENSE_FFN, V3_PREFILL, V3_SKEW)}
+# One GPU's share of an expert-parallel V3 prefill (8 GPUs, one expert group each): its 32
+# local experts receive about T*k rows, ~1024 per expert at T = 4096 per GPU; the shared
+# expert is replicated.  Emulated as a layer with 32 experts in 8 groups of 4, 4 kept.
+V3_EP_LOCAL = MoeShape("v3_ep_local", 5, 4096, 7168, 2048, 32, 8, 1, 2048, 8, 4)
+SHAPES = {s.name: s for s in (TINY, V3_DECODE, DENSE_FFN, V3_PREFILL, V3_SKEW, V3_EP_LOCAL)}
 
 
 def with_tokens(shape: MoeShape, tokens: int) -> MoeShape:

@@ -146,3 +146,15 @@ def test_dense_ffn_sampled_tokens():
     xb = synth.gen_x(s)
     got = _run(layer, xb)
     _compare_router_run(layer, xb, got, tokens=[0, 1234, 4095])
+
+
+def test_ep_local_sampled_tokens():
+    """One GPU's share of an expert-parallel V3 prefill: 32 local experts, ~1024 rows each."""
+    s = synth.V3_EP_LOCAL
+    say(f"forward {s.name} T={s.tokens} E={s.n_experts} (sampled oracle check)")
+    layer = Layer(s)
+    xb = synth.gen_x(s)
+    got = _run(layer, xb)
+    counts = np.bincount(got["topk_idx"].reshape(-1), minlength=s.n_experts)
+    say(f"  rows per expert: min {counts.min()}, max {counts.max()}")
+    _compare_router_run(layer, xb, got, tokens=_sample(got["topk_idx"], 4, s.cfg_id))
