@@ -341,7 +341,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_decode")
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=14)   # ~10 s of oracle work at decode shapes
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--ue8m0", action="store_true", help="power-of-two (UE8M0) scales for weights and activations")
