@@ -115,11 +115,17 @@ GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/launch.h")
 
 
 def gemm_source_hash() -> str:
+    """SHA-256 of the GEMM sources with comments and blank space removed, so that a comment
+    edit keeps the stored counters while any change to the code drops them."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "sparse_moe_ffn_sigmoid_amd", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_moe_ffn_sigmoid_amd", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -389,15 +389,17 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // MFMA tile kernel for groups of many rows (prefill, dense layers).
-// Workgroup: 4 waves as 2 (rows) x 2 (columns); tile 32*MT rows x 256 B rows
-// (plain: 256 output columns; SwiGLU: 128 gate + 128 up rows = one 128-column
-// h tile).  Wave tile: 16*MT rows x 128 B rows (MT x 8 MFMA tiles).
+// Workgroup: WM x WN waves (2 x 2, or 2 x 4 for tiles of 64+ rows); tile
+// 16*MT*WM rows x 256 B rows (plain: 256 output columns; SwiGLU: 128 gate +
+// 128 up rows = one 128-column h tile).  Wave tile: 16*MT rows x 256/WN B rows.
 // Staging: A and B tiles of a K block go global -> LDS directly
-// (global_load_lds_dwordx4: each wave load writes 1 KB of LDS) in fragment
-// order, so every MFMA operand read is one 1 KB-contiguous ds_read_b128 at an
-// immediate offset; 3 LDS stages, one barrier per K block.  Per K block each
-// wave issues the same number of loads (kLoads), so "my loads for block kb are
-// done" is a constant vmcnt.
+// (global_load_lds_dwordx4: each wave load writes 1 KB of LDS).  B arrives in
+// fragment order, so each B operand read is one 1 KB-contiguous ds_read_b128;
+// A arrives as whole 128-byte rows (8 rows per wave load) with the 16-byte
+// chunk index XORed by (row & 7), which keeps the 16 lanes of a ds_read_b128
+// phase on distinct banks.  3 LDS stages, one barrier per K block.  Per K block
+// each wave issues the same number of loads (kLoads), so "my loads for block
+// kb are done" is a constant vmcnt.
 constexpr int kStages = 3;
 
 __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base) {
