@@ -218,12 +218,16 @@ def _gemm_case(seed, M_groups, N, K, gather_rows=None):
     return a_q, a_s, b_q, b_s, offsets, gather
 
 
+# Group sizes pick the kernel: <= 16 rows on average the weight-streaming kernel, else the LDS
+# tile kernel with 32-, 64- or 128-row tiles.
 GEMM_CASES = [
     ([16], 128, 128, None),
     ([1, 0, 37, 5, 130, 0, 64], 256, 384, None),
     ([300, 2, 0, 77], 512, 256, 120),
     ([2000], 384, 512, None),
     ([3] * 40, 256, 256, 50),
+    ([100, 0, 129, 255, 7, 160], 384, 640, None),   # 128-row tiles: partial column tile, K tail of 2
+    ([70, 90], 256, 128, 60),                        # 128-row tiles, one K block
 ]
 
 
@@ -240,9 +244,9 @@ def test_grouped_gemm_store_f32(case):
     assert np.all(np.abs(got - ref) <= FP8_MFMA_REL * _absdot(a_q, a_s, gat, b_q, b_s, off) + 1e-30)
 
 
-def test_grouped_gemm_bf16_and_scatter():
-    say("grouped GEMM bf16 + weighted scatter-add")
-    mg = [5, 0, 70, 33]
+@pytest.mark.parametrize("mg", [[5, 0, 70, 33], [70, 100, 0, 90]])
+def test_grouped_gemm_bf16_and_scatter(mg):
+    say(f"grouped GEMM bf16 + weighted scatter-add groups={mg}")
     N, K = 256, 256
     a_q, a_s, b_q, b_s, off, _ = _gemm_case(77, mg, N, K)
     args = [to_dev(a_q), to_dev(a_s), _packed(b_q), to_dev(b_s), to_dev(off)]
@@ -265,7 +269,8 @@ def test_grouped_gemm_bf16_and_scatter():
 
 
 @pytest.mark.parametrize("mg,W,K,wide", [([7, 0, 130], 128, 256, False), ([64] * 5, 256, 512, False),
-                                         ([1000], 128, 384, False), ([40, 90], 128, 256, True)])
+                                         ([1000], 128, 384, False), ([40, 90], 128, 256, True),
+                                         ([130, 0, 75, 200], 256, 768, False), ([66, 128], 128, 128, False)])
 def test_grouped_gemm_swiglu_quant(mg, W, K, wide):
     say(f"grouped GEMM SwiGLU+quant groups={mg} W={W} K={K} full-range codes={wide}")
     a_q, a_s, b_q, b_s, off, _ = _gemm_case(W + K, mg, 2 * W, K)
