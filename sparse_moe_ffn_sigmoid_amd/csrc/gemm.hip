@@ -198,7 +198,10 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   __shared__ float red[4][16];
   __shared__ __attribute__((aligned(16))) uint8_t stage[16 * 128];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
+  // wave index made wave-uniform: the MFMAs below sit under branches on it, and an MFMA writes
+  // every lane whatever EXEC holds, so those branches must be scalar
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r16 = lane & 15,
+            q = lane >> 4;
   int si, g, m0, m_end;
   if (!find_tile(args, 16, scan_tmp, pre, pick, si, g, m0, m_end)) return;
   const GemmSeg& s0 = args.seg[0];

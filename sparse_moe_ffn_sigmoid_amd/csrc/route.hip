@@ -22,7 +22,9 @@ __global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* 
                                                                 const uint16_t* __restrict__ w, int T, int E, int D,
                                                                 float* __restrict__ scores) {
   __shared__ v4f part[NW][MTK * NT][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform wave index: the K-step bounds derive from it and guard MFMAs, which write every
+  // lane whatever EXEC holds, so those branches must be scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r16 = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * 16 * MTK, e0 = blockIdx.y * 16 * NT;
   const int steps = D >> 5;                     // 32-wide K steps, split as evenly as possible
@@ -56,14 +58,26 @@ __global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* 
         for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][u], b[j][u], acc[i][j], 0, 0, 0);
   }
-  for (; k < s1; ++k) {
+  if (k < s1) {                                 // the last, partial batch: all its loads first
+    v8bf a[MTK][U] = {}, b[NT][U] = {};
 #pragma unroll
-    for (int i = 0; i < MTK; ++i) {
-      const v8bf a = *reinterpret_cast<const v8bf*>(xa[i] + 32 * k);
+    for (int u = 0; u < U; ++u) {
+      if (k + u < s1) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, *reinterpret_cast<const v8bf*>(wb[j] + 32 * k),
-                                                            acc[i][j], 0, 0, 0);
+        for (int i = 0; i < MTK; ++i) a[i][u] = *reinterpret_cast<const v8bf*>(xa[i] + 32 * (k + u));
+#pragma unroll
+        for (int j = 0; j < NT; ++j) b[j][u] = *reinterpret_cast<const v8bf*>(wb[j] + 32 * (k + u));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k + u < s1) {
+#pragma unroll
+        for (int i = 0; i < MTK; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][u], b[j][u], acc[i][j], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -133,38 +147,46 @@ __global__ __launch_bounds__(256) void route_reg_kernel(const float* __restrict_
     rank += (o > gscore || (o == gscore && g < mygroup)) ? 1 : 0;
   }
   const bool kept = live && rank < gk;
+  // each round's winner carries its unbiased score along, so the weights need no second
+  // read of the scores
   unsigned taken = 0;
   int mine = 0;
+  float mine_s = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float best = -INFINITY;
+    float best = -INFINITY, best_s = 0.0f;
     int bi = INT_MAX;
     if (kept) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         if (!((taken >> i) & 1u) && (b[i] > best || bi == INT_MAX)) {
           best = b[i];
+          best_s = sv[i];
           bi = e0 + i;
         }
       }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o);
+      const float ov = __shfl_xor(best, o), os = __shfl_xor(best_s, o);
       const int oi = __shfl_xor(bi, o);
       if (ov > best || (ov == best && oi < bi)) {
         best = ov;
+        best_s = os;
         bi = oi;
       }
     }
     if (bi == INT_MAX) bi = 0;                      // only with NaN scores, outside the contract
     if (bi >= e0 && bi < e0 + EPL) taken |= 1u << (bi - e0);
-    if (lane == j) mine = bi;
+    if (lane == j) {
+      mine = bi;
+      mine_s = best_s;
+    }
   }
   float sum = 0.0f;
-  for (int j = 0; j < k; ++j) sum += s[__shfl(mine, j)];
+  for (int j = 0; j < k; ++j) sum += __shfl(mine_s, j);
   if (lane < k) {
     topk_idx[(long)t * k + lane] = mine;
-    topk_w[(long)t * k + lane] = (s[mine] / sum) * routed_scale;
+    topk_w[(long)t * k + lane] = (mine_s / sum) * routed_scale;
   }
 }
 
