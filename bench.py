@@ -24,6 +24,8 @@ Helpers for the counter runs:
   --traffic-summary DIR    turns the four counter runs under DIR (fetch/, write/, copy_fetch/,
                            copy_write/; commands in the written file) into
                            profiles/<workload>_gate_up_traffic.md.
+  --mfma-summary DIR       turns the MFMA counter run under DIR (mfma/) and a bench line
+                           (DIR/bench.json) into profiles/<workload>_mfma_utilization.md.
 """
 from __future__ import annotations
 
@@ -186,6 +188,70 @@ def _counter_means(d: str, counter: str, substr: str):
     if not vals:
         raise SystemExit(f"no {counter} rows for kernels matching {substr!r} under {d}")
     return sum(vals) / len(vals), len(vals)
+
+
+def _gemm_flops(shape):
+    """Algorithmic FLOPs of the gate/up and the down grouped GEMM of one layer call."""
+    cols = shape.top_k * shape.inter if shape.n_experts else 0
+    cols += shape.n_shared * shape.inter_shared
+    gu = 2.0 * shape.tokens * shape.hidden * 2 * cols
+    return gu, gu / 2
+
+
+def mfma_summary(d: str, shape) -> None:
+    """MFMA utilisation of the two grouped GEMMs from one rocprofv3 counter run: busy fraction of
+    the MFMA pipes (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of the dispatch; GRBM_GUI_ACTIVE
+    counts the dispatch's cycles once per XCD, so it is divided by the 8 XCDs), pipe cycles per
+    MFMA instruction, the clock the counters imply, and the kernels' FLOP rate at the live
+    durations of the bench line in DIR/bench.json."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(d, "mfma", "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = r["Kernel_Name"]
+            if "gemm_kernel" not in k:
+                continue
+            e = per.setdefault(k.split("(")[0].replace("void ", "").replace("moefp8::", ""), {})
+            e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            e.setdefault("_ns", {})[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not per:
+        raise SystemExit(f"no GEMM rows under {d}/mfma")
+    live = json.loads(open(os.path.join(d, "bench.json")).read().strip().splitlines()[-1])
+    gu, dn = _gemm_flops(shape)
+    cmd = f"python3 $R/bench.py --workload {shape.name} --steps 3 --warmup 1 --no-cpu-baseline"
+    lines = [
+        f"# MFMA utilisation of the grouped GEMMs, {shape.name}", "",
+        "Commands (R = repository root; the counter run from `cd /tmp && export TMPDIR=/tmp`):", "", "```",
+        f"timeout -s KILL 120 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE "
+        f"-f csv -d $R/gpurun_out/mfma/mfma -o mfma -- {cmd}",
+        f"python3 $R/bench.py --workload {shape.name} --steps 20 --no-cpu-baseline > $R/gpurun_out/mfma/bench.json",
+        f"python3 bench.py --workload {shape.name} --mfma-summary gpurun_out/mfma", "```", "",
+        "busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs): the fraction of SIMD-cycles",
+        "in which the MFMA pipe works. The exact gate/up path runs bf16 16x16x32 MFMAs (16 pipe cycles,",
+        "1024 FLOP per cycle and SIMD: its own peak is half the FP8 one); the down GEMM FP8 16x16x128",
+        "(32 cycles, 2048 FLOP per cycle). Durations under the profiler run longer than live ones; the",
+        "FLOP rates use the live stage times of the bench line (HIP events on the launch stream).", "",
+        "| kernel | dispatches | busy | cycles/MFMA | clock GHz (counters) | live ms | TFLOP/s | % FP8 peak |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for name, e in sorted(per.items()):
+        n = len(e["SQ_INSTS_MFMA"])
+        busy = sum(e["SQ_VALU_MFMA_BUSY_CYCLES"]) / n
+        inst = sum(e["SQ_INSTS_MFMA"]) / n
+        grbm = sum(e["GRBM_GUI_ACTIVE"]) / n
+        ns = sum(e["_ns"].values()) / len(e["_ns"])
+        frac = busy / (grbm / 8 * 1024)
+        is_gu = name.endswith(", 2>")
+        ms = live["stages_ms"]["gate_up_gemm" if is_gu else "down_gemm"]
+        fl = gu if is_gu else dn
+        tf = fl / (ms * 1e-3) / 1e12
+        lines.append(f"| `{name}` ({'gate/up' if is_gu else 'down'}) | {n} | {100 * frac:.1f}% | {busy / inst:.1f} | "
+                     f"{grbm / 8 / ns:.2f} | {ms:.3f} | {tf:.0f} | {100 * tf / FP8_PEAK_TFLOPS:.1f} |")
+    out = os.path.join(ROOT, "profiles", f"{shape.name}_mfma_utilization.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
 
 
 def traffic_summary(d: str, shape) -> None:
@@ -354,7 +420,12 @@ def main():
     ap.add_argument("--rmsnorm", action="store_true", help="the RMSNorm in front, fused with x's quantisation")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB")
     ap.add_argument("--traffic-summary", metavar="DIR")
+    ap.add_argument("--mfma-summary", metavar="DIR")
     args = ap.parse_args()
+    if args.mfma_summary:
+        import synth
+        mfma_summary(args.mfma_summary, synth.SHAPES[args.workload])
+        return
     if args.traffic_summary:
         import synth
         traffic_summary(args.traffic_summary, synth.SHAPES[args.workload])
