@@ -32,60 +32,69 @@
 //
 // Grouped rows: a static segment (the shared expert, or a plain GEMM) and a
 // dynamic segment (routed experts, rows given by device-side offsets) share
-// one launch; each workgroup finds its tile with an in-LDS prefix sum over the
-// groups' tile counts, and workgroups past the real tile count exit at once,
-// so no device-to-host copy of the counts is needed.
+// one launch; each wave finds its workgroup's tile with a cross-lane prefix sum
+// over the groups' tile counts, and workgroups past the real tile count exit at
+// once, so no device-to-host copy of the counts is needed.
 #include "common.h"
 #include "launch.h"
 
 namespace moefp8 {
 
-// Inclusive prefix over the dynamic segment's per-group tile counts
-// ceil(rows_g / bm) into pre[0..G-1] (G <= 1024, 256 threads); returns the total.
-__device__ int group_tile_prefix(const GemmSeg& sd, int bm, int* scan_tmp, int* pre) {
-  const int tid = threadIdx.x;
-  const int G = sd.G;
-  const int per = (G + 255) >> 8;               // groups per thread (G <= 1024)
-  int cnt[4];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gi = tid * per + i;
-    cnt[i] = 0;
-    if (i < per && gi < G) cnt[i] = (sd.offsets[gi + 1] - sd.offsets[gi] + bm - 1) / bm;
-    local += cnt[i];
-  }
-  scan_tmp[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int add = tid >= o ? scan_tmp[tid - o] : 0;
-    __syncthreads();
-    scan_tmp[tid] += add;
-    __syncthreads();
-  }
-  int run = scan_tmp[tid] - local;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gi = tid * per + i;
-    run += cnt[i];
-    if (i < per && gi < G) pre[gi] = run;       // inclusive prefix
-  }
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(scan_tmp[255]);
+// Tiles of the dynamic segment: group g has ceil(rows_g / bm) tiles of bm rows.  Each wave
+// scans the per-group counts on its own, with cross-lane shuffles (no LDS, no barrier; every
+// wave of a workgroup gets the same result): lane l owns groups l * per .. l * per + per - 1.
+struct GroupTiles {
+  int per;        // groups per lane (G <= 1024)
+  int first;      // this lane's first tile: the tiles of all groups of the lanes below it
+  int total;      // tiles of all groups (wave-uniform)
+};
+
+__device__ __forceinline__ int group_tiles(const GemmSeg& sd, int gi, int bm) {
+  return (sd.offsets[gi + 1] - sd.offsets[gi] + bm - 1) / bm;
 }
 
-// First group g with pre[g] > v (pre inclusive, non-decreasing); thread 0 searches, all read.
-__device__ int find_group(const int* pre, int G, int v, int* pick) {
-  if (threadIdx.x == 0) {
-    int lo = 0, hi = G;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (pre[mid] > v) hi = mid; else lo = mid + 1;
-    }
-    pick[0] = lo;
+__device__ GroupTiles scan_group_tiles(const GemmSeg& sd, int bm) {
+  const int lane = threadIdx.x & 63;
+  const int per = (sd.G + 63) >> 6;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int gi = lane * per + i;
+    if (gi < sd.G) sum += group_tiles(sd, gi, bm);
   }
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(pick[0]);
+  int inc = sum;                                // inclusive scan over the lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  GroupTiles r;
+  r.per = per;
+  r.first = inc - sum;
+  r.total = __builtin_amdgcn_readlane(inc, 63);
+  return r;
+}
+
+// The group holding tile t (< total), its first tile and its tile count, all wave-uniform.
+// The owning lane is the last one whose first tile is <= t (first tiles never decrease).
+__device__ void locate_tile(const GemmSeg& sd, int bm, const GroupTiles& s, int t, int& g, int& start, int& count) {
+  const unsigned long long m = __ballot(s.first <= t);
+  const int L = __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m));
+  int acc = __builtin_amdgcn_readlane(s.first, L);
+  g = L * s.per;
+  count = 0;
+  for (int i = 0; i < s.per; ++i) {
+    const int gi = L * s.per + i;
+    const int c = group_tiles(sd, gi, bm);
+    if (t < acc + c) {
+      g = gi;
+      count = c;
+      break;
+    }
+    acc += c;
+  }
+  g = __builtin_amdgcn_readfirstlane(g);
+  start = __builtin_amdgcn_readfirstlane(acc);
+  count = __builtin_amdgcn_readfirstlane(count);
 }
 
 // Maps blockIdx.x to (segment, group, first row, end row) for tiles of bm
@@ -94,8 +103,7 @@ __device__ int find_group(const int* pre, int G, int v, int* pick) {
 // tile count.  The tile coordinates are workgroup-uniform: readfirstlane lets
 // the compiler keep them (and every address derived from them) in scalar
 // registers.
-__device__ bool find_tile(const GemmArgs& args, int bm, int* scan_tmp, int* pre, int* pick, int& si, int& g, int& m0,
-                          int& m_end) {
+__device__ bool find_tile(const GemmArgs& args, int bm, int& si, int& g, int& m0, int& m_end) {
   int v = blockIdx.x;
   if (v < args.seg[0].m_tiles) {
     si = 0;
@@ -107,12 +115,12 @@ __device__ bool find_tile(const GemmArgs& args, int bm, int* scan_tmp, int* pre,
   v -= args.seg[0].m_tiles;
   const GemmSeg& sd = args.seg[1];
   if (v >= sd.m_tiles) return false;
-  const int total = group_tile_prefix(sd, bm, scan_tmp, pre);
-  if (v >= total) return false;
-  g = find_group(pre, sd.G, v, pick);
+  const GroupTiles scan = scan_group_tiles(sd, bm);
+  if (v >= scan.total) return false;
+  int start, count;
+  locate_tile(sd, bm, scan, v, g, start, count);
   si = 1;
-  const int tiles_g = (sd.offsets[g + 1] - sd.offsets[g] + bm - 1) / bm;
-  m0 = __builtin_amdgcn_readfirstlane(sd.offsets[g] + (v - (pre[g] - tiles_g)) * bm);
+  m0 = __builtin_amdgcn_readfirstlane(sd.offsets[g] + (v - start) * bm);
   m_end = __builtin_amdgcn_readfirstlane(sd.offsets[g + 1]);
   return true;
 }
@@ -143,12 +151,14 @@ __device__ __forceinline__ void panel_map(int L, int c, int ny, int& mt, int& nt
   }
 }
 
-__device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int* scan_tmp, int* pre, int* pick,
-                          int& si, int& g, int& m0, int& m_end, int& nt) {
+__device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& si, int& g, int& m0, int& m_end,
+                          int& nt) {
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& sd = args.seg[1];
   const int w0 = s0.m_tiles * ny0;
-  const int c1 = sd.m_tiles > 0 ? group_tile_prefix(sd, bm, scan_tmp, pre) : 0;
+  GroupTiles scan{0, 0, 0};
+  if (sd.m_tiles > 0) scan = scan_group_tiles(sd, bm);
+  const int c1 = scan.total;
   const int total = w0 + c1 * ny1;
   const int chunk = (total + 7) >> 3;
   const int b = blockIdx.x, j = b >> 3;
@@ -164,9 +174,9 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int* s
     m_end = s0.m_rows;
   } else {
     const int v = w - w0;
-    g = find_group(pre, sd.G, v / ny1, pick);
-    const int c = (sd.offsets[g + 1] - sd.offsets[g] + bm - 1) / bm;
-    panel_map(v - ny1 * (pre[g] - c), c, ny1, mt, nt);
+    int start, c;
+    locate_tile(sd, bm, scan, v / ny1, g, start, c);
+    panel_map(v - ny1 * start, c, ny1, mt, nt);
     si = 1;
     m0 = sd.offsets[g] + mt * bm;
     m_end = sd.offsets[g + 1];
@@ -192,9 +202,6 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   constexpr int NF = NB * NTW;                 // B fragments per lane per K block
   constexpr int CW = 16 * NTW;                 // columns per wave in each B block
   constexpr bool kExact = EPI == kEpiSwiglu;
-  __shared__ int scan_tmp[256];
-  __shared__ int pre[1024];
-  __shared__ int pick[1];
   __shared__ float red[4][16];
   __shared__ __attribute__((aligned(16))) uint8_t stage[16 * 128];
 
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r16 = lane & 15,
             q = lane >> 4;
   int si, g, m0, m_end;
-  if (!find_tile(args, 16, scan_tmp, pre, pick, si, g, m0, m_end)) return;
+  if (!find_tile(args, 16, si, g, m0, m_end)) return;
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& s1 = args.seg[1];
   const int K = si ? s1.K : s0.K, nkb = K >> 7;
@@ -448,9 +455,6 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGE];
-  __shared__ int scan_tmp[256];
-  __shared__ int pre[1024];
-  __shared__ int pick[1];
   __shared__ float red[WN][BM];
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
@@ -461,7 +465,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   const int ny0 = kExact ? s0.N / 256 : (s0.N + 255) / 256;   // n tiles per segment
   const int ny1 = kExact ? s1.N / 256 : (s1.N + 255) / 256;
   int si, g, m0, m_end, nt;
-  if (!find_work(args, BM, ny0, ny1, scan_tmp, pre, pick, si, g, m0, m_end, nt)) return;
+  if (!find_work(args, BM, ny0, ny1, si, g, m0, m_end, nt)) return;
   const int K = si ? s1.K : s0.K, nkb = K >> 7;
   const int Nfull = si ? s1.N : s0.N;
   const int half = Nfull / (kExact ? 2 : 1);
