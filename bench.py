@@ -222,11 +222,11 @@ def mfma_summary(d: str, shape) -> None:
     cmd = f"python3 $R/bench.py --workload {shape.name} --steps 3 --warmup 1 --no-cpu-baseline"
     lines = [
         f"# MFMA utilisation of the grouped GEMMs, {shape.name}", "",
-        "Commands (R = repository root; the counter run from `cd /tmp && export TMPDIR=/tmp`):", "", "```",
+        "Commands (R = repository root, OUT = the directory the runs write to; the counter run from `cd /tmp && export TMPDIR=/tmp`):", "", "```",
         f"timeout -s KILL 120 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE "
-        f"-f csv -d $R/gpurun_out/mfma/mfma -o mfma -- {cmd}",
-        f"python3 $R/bench.py --workload {shape.name} --steps 20 --no-cpu-baseline > $R/gpurun_out/mfma/bench.json",
-        f"python3 bench.py --workload {shape.name} --mfma-summary gpurun_out/mfma", "```", "",
+        f"-f csv -d $OUT/mfma -o mfma -- {cmd}",
+        f"python3 $R/bench.py --workload {shape.name} --steps 20 --no-cpu-baseline > $OUT/bench.json",
+        f"python3 bench.py --workload {shape.name} --mfma-summary $OUT", "```", "",
         "busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs): the fraction of SIMD-cycles",
         "in which the MFMA pipe works. The exact gate/up path runs bf16 16x16x32 MFMAs (16 pipe cycles,",
         "1024 FLOP per cycle and SIMD: its own peak is half the FP8 one); the down GEMM FP8 16x16x128",
@@ -264,18 +264,18 @@ def traffic_summary(d: str, shape) -> None:
     ff, fw = (n + 4 * COPY_MIB) / (f_c * 1024), n / (w_c * 1024)
     traffic = f_k * 1024 * ff + w_k * 1024 * fw
     bench = f"python3 $R/bench.py --workload {shape.name} --steps 3 --warmup 1 --no-cpu-baseline"
-    run = "timeout -s KILL 90 rocprofv3 --pmc {c} -f csv -d $R/gpurun_out/traffic/{o} -o {o} -- {cmd}"
+    run = "timeout -s KILL 90 rocprofv3 --pmc {c} -f csv -d $OUT/traffic/{o} -o {o} -- {cmd}"
     lines = [
         f"# HBM traffic of the gate/up GEMM kernel, {shape.name}",
         "",
-        "Counter runs (one counter per run, R = repository root, from `cd /tmp && export TMPDIR=/tmp`):",
+        "Counter runs (one counter per run, R = repository root, OUT = the directory the runs write to, from `cd /tmp && export TMPDIR=/tmp`):",
         "",
         "```",
         run.format(c="FETCH_SIZE", o="fetch", cmd=bench),
         run.format(c="WRITE_SIZE", o="write", cmd=bench),
         run.format(c="FETCH_SIZE", o="copy_fetch", cmd=f"python3 $R/bench.py --calibrate-copy {COPY_MIB}"),
         run.format(c="WRITE_SIZE", o="copy_write", cmd=f"python3 $R/bench.py --calibrate-copy {COPY_MIB}"),
-        f"python3 bench.py --workload {shape.name} --traffic-summary gpurun_out/traffic",
+        f"python3 bench.py --workload {shape.name} --traffic-summary $OUT/traffic",
         "```",
         "",
         f"Kernel: `{kern}` ({n_f} and {n_w} dispatches). Counters are KiB per dispatch.",
