@@ -25,18 +25,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float f) {
   const uint32_t u = __float_as_uint(f);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a > 0x7F800000u) {
-    code = 0x7Fu;                                   // NaN
-  } else if (a >= 0x43E00000u) {
-    code = 0x7Eu;                                   // >= 448 (and inf): saturate
-  } else if (a >= 0x3C800000u) {                    // >= 2^-6: normal
-    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // (exp32 << 3 | m3), carry included
-    code = r - (120u << 3);                         // exponent bias 127 -> 7
-    code = code > 0x7Eu ? 0x7Eu : code;
-  } else {
-    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);          // multiples of 2^-9, 0..8
-  }
+  // every range's code is computed and the right one selected (no branches: a per-value branch
+  // makes the lanes of a wave diverge and costs more than the extra arithmetic)
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;     // (exp32 << 3 | m3), carry included
+  const uint32_t rn = r - (120u << 3);                            // exponent bias 127 -> 7 (used when a >= 2^-6)
+  const uint32_t normal = rn > 0x7Eu ? 0x7Eu : rn;
+  const uint32_t sub = (uint32_t)rintf(__uint_as_float(a < 0x3C800000u ? a : 0u) * 512.0f);   // multiples of 2^-9, 0..8
+  uint32_t code = a >= 0x3C800000u ? normal : sub;                // >= 2^-6: normal
+  code = a >= 0x43E00000u ? 0x7Eu : code;                         // >= 448 (and inf): saturate
+  code = a > 0x7F800000u ? 0x7Fu : code;                          // NaN
   return code | sign;
 }
 

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = tid >> 4, sub = tid & 15;
   const int tpr = cols >> 7;
   const uint16_t* xr = x + row * ld_x;
-  uint4 keep[R];
+  uint4 keep[R], gkeep[R];                      // the row's x and gamma pieces (NT > 0)
   double hi = 0.0, lo = 0.0;
   auto accumulate = [&](const uint4 p) {
     const uint32_t w[4] = {p.x, p.y, p.z, p.w};
@@ -193,6 +193,11 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     for (int i = 0; i < NT; ++i) {
       const int tc = grp + 16 * i;
       keep[i] = tc < tpr ? *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
+      // gamma is read before the reduction, so its latency hides under the row's
+      gkeep[i] = tc < tpr ? *reinterpret_cast<const uint4*>(gamma + tc * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
       accumulate(keep[i]);                       // zeros add nothing
     }
   } else {
@@ -223,9 +228,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
   const double ss = hi + lo;
   const float inv = (float)(1.0 / sqrt(ss / (double)cols + (double)eps));
 
-  auto emit = [&](int tc, const uint4 px) {
+  auto emit = [&](int tc, const uint4 px, const uint4 pg) {
     const int c0 = tc * 128 + sub * 8;
-    const uint4 pg = *reinterpret_cast<const uint4*>(gamma + c0);
     const uint32_t wx[4] = {px.x, px.y, px.z, px.w}, wg[4] = {pg.x, pg.y, pg.z, pg.w};
     float v[8];
     uint32_t yb[4];
@@ -260,9 +264,11 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
   if constexpr (NT > 0) {
 #pragma unroll
     for (int i = 0; i < NT; ++i)
-      if (grp + 16 * i < tpr) emit(grp + 16 * i, keep[i]);     // uniform within each 16-lane group
+      if (grp + 16 * i < tpr) emit(grp + 16 * i, keep[i], gkeep[i]);   // uniform within each 16-lane group
   } else {
-    for (int tc = grp; tc < tpr; tc += 16) emit(tc, *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8));
+    for (int tc = grp; tc < tpr; tc += 16)
+      emit(tc, *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8),
+           *reinterpret_cast<const uint4*>(gamma + tc * 128 + sub * 8));
   }
 }
 
