@@ -15,26 +15,27 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// OCP E4M3FN encode of an fp32 value: round to nearest, ties to even mantissa,
-// sign kept, saturating at 448 (0x7E); NaN -> 0x7F.  Written from the format
-// definition: in the normal range (|f| >= 2^-6) the 23-bit fp32 fraction is
-// rounded to 3 bits by adding half an ulp minus one plus the kept lsb (round
-// half to even on the integer pattern) and the exponent is re-biased from 127
-// to 7; below 2^-6 the grid is the subnormal step 2^-9.
-__device__ __forceinline__ uint32_t e4m3_encode(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  // every range's code is computed and the right one selected (no branches: a per-value branch
-  // makes the lanes of a wave diverge and costs more than the extra arithmetic)
-  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;     // (exp32 << 3 | m3), carry included
-  const uint32_t rn = r - (120u << 3);                            // exponent bias 127 -> 7 (used when a >= 2^-6)
-  const uint32_t normal = rn > 0x7Eu ? 0x7Eu : rn;
-  const uint32_t sub = (uint32_t)rintf(__uint_as_float(a < 0x3C800000u ? a : 0u) * 512.0f);   // multiples of 2^-9, 0..8
-  uint32_t code = a >= 0x3C800000u ? normal : sub;                // >= 2^-6: normal
-  code = a >= 0x43E00000u ? 0x7Eu : code;                         // >= 448 (and inf): saturate
-  code = a > 0x7F800000u ? 0x7Fu : code;                          // NaN
-  return code | sign;
+// OCP E4M3FN encoding of two fp32 values: round to nearest, ties to even mantissa,
+// sign kept, saturating at 448 (0x7E), NaN -> 0x7F | sign.  The gfx950 conversion
+// instruction (v_cvt_pk_fp8_f32) rounds to nearest even into the OCP format; the
+// values are clamped to +-448 first (the format has no infinity, so saturation is
+// the clamp) and NaN inputs are patched after.  Returns code(a) | code(b) << 8.
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+  const uint32_t na = ((__float_as_uint(a) >> 24) & 0x80u) | 0x7Fu;
+  const uint32_t nb = ((__float_as_uint(b) >> 16) & 0x8000u) | 0x7F00u;
+  r = a != a ? (r & 0xFF00u) | na : r;
+  r = b != b ? (r & 0x00FFu) | nb : r;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t e4m3_encode(float f) { return e4m3_encode2(f, 0.0f) & 0xFFu; }
+
+// Codes of four values packed into a word, v0 in the low byte.
+__device__ __forceinline__ uint32_t e4m3_encode4(float v0, float v1, float v2, float v3) {
+  return e4m3_encode2(v0, v1) | (e4m3_encode2(v2, v3) << 16);
 }
 
 // Scale of one quantisation tile (amax >= 0): fp32(amax / 448), correctly rounded; or, with

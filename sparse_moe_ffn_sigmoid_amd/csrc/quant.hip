@@ -48,11 +48,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = group_max<16>(amax);
   const float sc = tile_scale(amax, pow2 != 0);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / sc) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / sc) << (8 * i);
+  const uint32_t lo = e4m3_encode4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+  const uint32_t hi = e4m3_encode4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
   if (valid) {
     *reinterpret_cast<uint2*>(q + r * ld_q + c0) = make_uint2(lo, hi);
     if (sub == 0) s[r * tpr + tc] = sc;
@@ -89,10 +86,8 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
     uint32_t wd[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) word |= e4m3_encode(v[16 * i + 4 * j + b] / sc) << (8 * b);
-      wd[j] = word;
+      const float* vv = v + 16 * i + 4 * j;
+      wd[j] = e4m3_encode4(vv[0] / sc, vv[1] / sc, vv[2] / sc, vv[3] / sc);
     }
     reinterpret_cast<uint4*>(dst)[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
@@ -252,11 +247,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = group_max<16>(amax);
     const float sc = tile_scale(amax, pow2 != 0);
-    uint32_t lo4 = 0, hi4 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo4 |= e4m3_encode(v[i] / sc) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi4 |= e4m3_encode(v[4 + i] / sc) << (8 * i);
+    const uint32_t lo4 = e4m3_encode4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+    const uint32_t hi4 = e4m3_encode4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
     if (y) *reinterpret_cast<uint4*>(y + row * ld_y + c0) = make_uint4(yb[0], yb[1], yb[2], yb[3]);
     *reinterpret_cast<uint2*>(q + row * ld_q + c0) = make_uint2(lo4, hi4);
     if (sub == 0) s[row * tpr + tc] = sc;
