@@ -141,35 +141,17 @@ hipError_t launch_quant_128x128(const float* w, int rows, int cols, uint8_t* q, 
   return hipGetLastError();
 }
 
-// RMSNorm fused with the 1x128 quantisation (llm-architectures-explained,
-// "DeepSeek-R1", facts rows "Norm placement" / "Norm type": RMSNorm right before
-// the MLP).  One workgroup (16 groups of 16 lanes) per row; group g handles the
-// 128-column tiles g, g + 16, ...; each lane 8 consecutive values of a tile.
-//   the sum of squares: squares of bf16 values are exact in fp64; they are
-//     accumulated in double-double (TwoSum) per lane and reduced pairwise, then
-//     rounded once, which gives the exactly rounded fp64 sum for any realistic
-//     row (so the result does not depend on the summation order);
-//   inv = fp32(1 / sqrt(sum / cols + eps)) in fp64;
-//   y = bf16(fp32(fp32(x * inv) * gamma)), written out if asked, and quantised
-//     per 128 columns like quant_1x128.
-// NT > 0: the row stays in registers between the two steps (NT tiles per group,
-// cols <= 16 * NT * 128), one read of x; NT == 0: any width, the second step
-// reads the row again (from L2).
-template <int NT>
-__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ gamma, float eps, int cols,
-                                                            int ld_x, uint16_t* __restrict__ y, int ld_y,
-                                                            uint8_t* __restrict__ q, int ld_q, float* __restrict__ s,
-                                                            int pow2) {
-  constexpr int R = NT > 0 ? NT : 1;
-  __shared__ double red_hi[4], red_lo[4];
-  const long row = blockIdx.x;
+// Exactly rounded fp64 sum of the squares of a bf16 row (cols = 128 * tpr), for the
+// workgroup of rmsnorm_quant_kernel: double-double (TwoSum) accumulation per lane, the
+// same through the wave and across the 4 waves (red_hi / red_lo: 4 doubles each in LDS).
+// Every thread returns the sum.  It runs only when the plain fp64 sum cannot decide the
+// fp32 result, and reads the row again from memory (L2) rather than from the caller's
+// registers, which keeps the common path's register count (and occupancy) as it is.
+__device__ __forceinline__ double exact_row_sum(const uint16_t* xr, int tpr, double* red_hi, double* red_lo) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = tid >> 4, sub = tid & 15;
-  const int tpr = cols >> 7;
-  const uint16_t* xr = x + row * ld_x;
-  uint4 keep[R], gkeep[R];                      // the row's x and gamma pieces (NT > 0)
   double hi = 0.0, lo = 0.0;
-  auto accumulate = [&](const uint4 p) {
+  for (int tc = grp; tc < tpr; tc += 16) {
+    const uint4 p = *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8);
     const uint32_t w[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -182,21 +164,6 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
         lo += e;
       }
     }
-  };
-  if constexpr (NT > 0) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int tc = grp + 16 * i;
-      keep[i] = tc < tpr ? *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
-      // gamma is read before the reduction, so its latency hides under the row's
-      gkeep[i] = tc < tpr ? *reinterpret_cast<const uint4*>(gamma + tc * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      accumulate(keep[i]);                       // zeros add nothing
-    }
-  } else {
-    for (int tc = grp; tc < tpr; tc += 16) accumulate(*reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -220,8 +187,85 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __re
     hi = t;
     lo = lo + red_lo[w2] + e;
   }
-  const double ss = hi + lo;
-  const float inv = (float)(1.0 / sqrt(ss / (double)cols + (double)eps));
+  return hi + lo;
+}
+
+// RMSNorm fused with the 1x128 quantisation (llm-architectures-explained,
+// "DeepSeek-R1", facts rows "Norm placement" / "Norm type": RMSNorm right before
+// the MLP).  One workgroup (16 groups of 16 lanes) per row; group g handles the
+// 128-column tiles g, g + 16, ...; each lane 8 consecutive values of a tile.
+//   the sum of squares: squares of bf16 values are exact in fp64.  The sum is
+//     first taken with plain fp64 adds; its relative error is below cols * 2^-53
+//     whatever the order, so fp32(inv) below is the one the exact sum gives
+//     unless the fp64 inv lies that close to a rounding midpoint of the fp32
+//     grid.  Then (rarely; a uniform branch for the workgroup) the sum is taken
+//     again in double-double (TwoSum per lane, pairwise reduction), which gives
+//     the exactly rounded fp64 sum for any realistic row, so the result never
+//     depends on the summation order;
+//   inv = fp32(1 / sqrt(sum / cols + eps)) in fp64;
+//   y = bf16(fp32(fp32(x * inv) * gamma)), written out if asked, and quantised
+//     per 128 columns like quant_1x128.
+// NT > 0: the row stays in registers between the two steps (NT tiles per group,
+// cols <= 16 * NT * 128), one read of x; NT == 0: any width, the second step
+// reads the row again (from L2).
+template <int NT>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ gamma, float eps, int cols,
+                                                            int ld_x, uint16_t* __restrict__ y, int ld_y,
+                                                            uint8_t* __restrict__ q, int ld_q, float* __restrict__ s,
+                                                            int pow2) {
+  constexpr int R = NT > 0 ? NT : 1;
+  __shared__ double red_hi[4], red_lo[4];
+  const long row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = tid >> 4, sub = tid & 15;
+  const int tpr = cols >> 7;
+  const uint16_t* xr = x + row * ld_x;
+  uint4 keep[R], gkeep[R];                      // the row's x and gamma pieces (NT > 0)
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int tc = grp + 16 * i;
+      keep[i] = tc < tpr ? *reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
+      // gamma is read before the reduction, so its latency hides under the row's
+      gkeep[i] = tc < tpr ? *reinterpret_cast<const uint4*>(gamma + tc * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // the row's sum of squares with plain fp64 adds
+  double hi = 0.0;
+  auto accumulate = [&](const uint4 p) {
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double a = (double)__uint_as_float(w[i] << 16), b = (double)__uint_as_float(w[i] & 0xFFFF0000u);
+      hi += a * a;
+      hi += b * b;
+    }
+  };
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) accumulate(keep[i]);       // zeros add nothing
+  } else {
+    for (int tc = grp; tc < tpr; tc += 16) accumulate(*reinterpret_cast<const uint4*>(xr + tc * 128 + sub * 8));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) hi += __shfl_xor(hi, o);
+  if (lane == 0) red_hi[wave] = hi;
+  __syncthreads();
+  const double ss_fast = ((red_hi[0] + red_hi[1]) + red_hi[2]) + red_hi[3];
+  const double inv64 = 1.0 / sqrt(ss_fast / (double)cols + (double)eps);
+  float inv = (float)inv64;
+  {
+    // distance of inv64 from the fp32 rounding midpoints on either side of inv, against a
+    // bound on the fast sum's effect (relative error < (cols / 2 + 3) * 2^-53 in inv64)
+    const uint32_t ib = __float_as_uint(inv);
+    const double below = 0.5 * ((double)inv + (double)__uint_as_float(ib - 1u));
+    const double above = 0.5 * ((double)inv + (double)__uint_as_float(ib + 1u));
+    const double margin = fmin(inv64 - below, above - inv64);
+    if (margin <= inv64 * ((double)cols * 0x1p-53 + 0x1p-50)) {   // same value in every thread
+      __syncthreads();                         // every thread has read the fast sum's partials
+      inv = (float)(1.0 / sqrt(exact_row_sum(xr, tpr, red_hi, red_lo) / (double)cols + (double)eps));
+    }
+  }
 
   auto emit = [&](int tc, const uint4 px, const uint4 pg) {
     const int c0 = tc * 128 + sub * 8;
