@@ -86,6 +86,9 @@ ROUTE_CASES = [
     (777, 64, 6, 8, 8, False, 0.2, 0),
     (500, 96, 4, 3, 2, True, 0.1, 1),
     (129, 1024, 16, 32, 4, False, 0.05, 0),
+    (1, 128, 64, 1, 1, False, 0.0, 0),        # the largest top_k, one group
+    (5, 64, 64, 4, 4, True, 0.1, 0),          # every expert chosen
+    (33, 1, 1, 1, 1, False, 0.0, 0),          # a single expert
 ]
 
 
@@ -102,7 +105,7 @@ def test_route_given_scores_bit_exact(case):
     assert np.array_equal(w.cpu().numpy().view(np.uint32), want_w.view(np.uint32))
 
 
-@pytest.mark.parametrize("shape", [synth.TINY, synth.with_tokens(synth.V3_PREFILL, 1000)])
+@pytest.mark.parametrize("shape", [synth.TINY, synth.V3_DECODE, synth.with_tokens(synth.V3_PREFILL, 1000)])
 def test_router_scores(shape):
     say(f"router scores {shape.name} T={shape.tokens}")
     xb = synth.gen_x(shape)
