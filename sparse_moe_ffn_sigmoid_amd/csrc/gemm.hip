@@ -135,6 +135,15 @@ __device__ bool find_tile(const GemmArgs& args, int bm, int& si, int& g, int& m0
 // dispatched to the 8 XCDs round-robin by workgroup id, so workgroup b runs
 // item (b % 8) * chunk + b / 8, and each XCD's L2 sees a contiguous run of
 // items (one expert's tiles land on one XCD and share its L2).
+//
+// Inside an XCD, workgroup j goes to shader engine j % 4 (measured on MI355X) and
+// the dispatch is in order: a shader engine whose CUs are all busy holds back
+// every later workgroup.  The m tiles of one n tile are therefore taken in an
+// order rotated by the number of whole 4-item rounds before that n tile, so
+// that each shader engine gets each m tile of a panel in turn.  The last m tile
+// of a group is often nearly empty and costs less than half a full one; with
+// two m tiles per group and no rotation, two shader engines would get every
+// full tile and the other two every partial one, and sit idle half the time.
 constexpr int kPanel = 4;
 
 __device__ __forceinline__ void panel_map(int L, int c, int ny, int& mt, int& nt) {
@@ -143,11 +152,11 @@ __device__ __forceinline__ void panel_map(int L, int c, int ny, int& mt, int& nt
   if (L < in_full) {
     const int p = L / (kPanel * ny), r = L - p * (kPanel * ny);
     nt = r / kPanel;
-    mt = p * kPanel + (r - nt * kPanel);
+    mt = p * kPanel + (r - nt * kPanel + nt) % kPanel;
   } else {
     const int rem = c - full * kPanel, r = L - in_full;
     nt = r / rem;
-    mt = full * kPanel + (r - nt * rem);
+    mt = full * kPanel + (r - nt * rem + rem * nt / 4) % rem;
   }
 }
 
@@ -459,13 +468,19 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loads below
-  const int wm = wave % WM, wn = wave / WM;
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& s1 = args.seg[1];
   const int ny0 = kExact ? s0.N / 256 : (s0.N + 255) / 256;   // n tiles per segment
   const int ny1 = kExact ? s1.N / 256 : (s1.N + 255) / 256;
   int si, g, m0, m_end, nt;
   if (!find_work(args, BM, ny0, ny1, si, g, m0, m_end, nt)) return;
+  // Wave (wm, wn) computes row block wm and column block wn of the tile.  A partial tile (the last
+  // tile of a group often is) takes wm = wave / WN: waves are placed on the CU's 4 SIMDs round-robin
+  // by wave index, so every SIMD then holds waves of both row halves, and the work left when the
+  // rows end in the first half is spread over all four SIMDs.  Full tiles keep wm = wave % WM,
+  // measured a few percent faster for them.
+  const bool partial = m_end - m0 < BM;
+  const int wm = partial ? wave / WN : wave % WM, wn = partial ? wave % WN : wave / WM;
   const int K = si ? s1.K : s0.K, nkb = K >> 7;
   const int Nfull = si ? s1.N : s0.N;
   const int half = Nfull / (kExact ? 2 : 1);
@@ -542,13 +557,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 #pragma unroll
     for (int f = 0; f < NTW; ++f) acc[mi][f] = v4f{0.f, 0.f, 0.f, 0.f};
   const int lane_off = lane * 16;
-  // A wave whose rows all lie past the group's end (the last tile of a group is often partial)
-  // only loads and synchronises; one uniform branch around the whole K block keeps the MFMA
-  // schedule inside it intact.
-  const bool wave_has_rows = m0 + wm * 16 * MT < m_end;
+  // In a partial tile a wave computes only its 16-row blocks that hold rows of the group (uniform
+  // branches between row blocks; full tiles run a copy of the K loop without them), and a wave
+  // with none of them only loads and synchronises.
+  const int nmi = __builtin_amdgcn_readfirstlane(min(MT, max(0, (m_end - m0 - wm * 16 * MT + 15) / 16)));
+  const bool wave_has_rows = nmi > 0;
 
   // MFMAs and scale promotion of one K block from the LDS stage at st (+ this lane's offset)
-  auto compute = [&](const uint8_t* st) {
+  auto compute = [&](const uint8_t* st, bool skip) __attribute__((always_inline)) {
     const uint8_t* const stb = st - lane_off;
     auto load_a = [&](int mi) {
       const int ab = wm * MT + mi;
@@ -575,6 +591,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
     }
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
+      if (skip && mi > 0 && mi >= nmi) break;   // the wave's remaining row blocks lie past the group's end
       const int ab = wm * MT + mi;
       const v8i af = af_next;
       if (mi + 1 < MT) af_next = load_a(mi + 1);
@@ -623,34 +640,40 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   // inside: with control flow in the loop body the compiler's wait insertion loses track of
   // which stage a pending LDS-DMA load writes and waits for all of them before LDS reads.
   // The last one to four blocks run in a peeled tail with the bounds checks.
-#define MFMA_STEP(kb_, cur_, nxt_)                                                                    \
+#define MFMA_STEP(kb_, cur_, nxt_, skip_)                                                             \
   {                                                                                                   \
     wait_vmcnt<kLoads>();                                                                             \
     block_barrier();                                                                                  \
     MFMA_ISSUE((kb_) + 2, nxt_);                                                                      \
-    if (wave_has_rows) compute((cur_) + lane_off);                                                    \
+    if (wave_has_rows) compute((cur_) + lane_off, skip_);                                             \
   }
-#define MFMA_STEP_TAIL(kb_, cur_, nxt_)                                                               \
+#define MFMA_STEP_TAIL(kb_, cur_, nxt_, skip_)                                                        \
   {                                                                                                   \
     const int kbs = (kb_);                                                                            \
     if (kbs + 1 < nkb) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();                                    \
     block_barrier();                                                                                  \
     if (kbs + 2 < nkb) MFMA_ISSUE(kbs + 2, nxt_);                                                     \
-    if (wave_has_rows) compute((cur_) + lane_off);                                                    \
+    if (wave_has_rows) compute((cur_) + lane_off, skip_);                                             \
+  }
+#define MFMA_KLOOP(skip_)                                                                             \
+  {                                                                                                   \
+    MFMA_ISSUE(0, smem0);                                                                             \
+    MFMA_ISSUE(nkb > 1 ? 1 : 0, smem1);  /* unconditional (no branch before the loop); for nkb == 1  \
+                                            a copy of block 0 that is never read */                   \
+    int kb0 = 0;                                                                                      \
+    for (; kb0 + 4 < nkb; kb0 += 3) {    /* every step here issues block kb + 2 < nkb */              \
+      MFMA_STEP(kb0, smem0, smem2, skip_);                                                            \
+      MFMA_STEP(kb0 + 1, smem1, smem0, skip_);                                                        \
+      MFMA_STEP(kb0 + 2, smem2, smem1, skip_);                                                        \
+    }                                                                                                 \
+    MFMA_STEP_TAIL(kb0, smem0, smem2, skip_);  /* 1 to 4 blocks remain; kb0 is a multiple of 3 */     \
+    if (kb0 + 1 < nkb) MFMA_STEP_TAIL(kb0 + 1, smem1, smem0, skip_);                                  \
+    if (kb0 + 2 < nkb) MFMA_STEP_TAIL(kb0 + 2, smem2, smem1, skip_);                                  \
+    if (kb0 + 3 < nkb) MFMA_STEP_TAIL(kb0 + 3, smem0, smem2, skip_);                                  \
   }
 
-  MFMA_ISSUE(0, smem0);
-  MFMA_ISSUE(nkb > 1 ? 1 : 0, smem1);           // unconditional (no branch before the loop); for
-  int kb0 = 0;                                  // nkb == 1 a copy of block 0 that is never read
-  for (; kb0 + 4 < nkb; kb0 += 3) {             // every step here issues block kb + 2 < nkb
-    MFMA_STEP(kb0, smem0, smem2);
-    MFMA_STEP(kb0 + 1, smem1, smem0);
-    MFMA_STEP(kb0 + 2, smem2, smem1);
-  }
-  MFMA_STEP_TAIL(kb0, smem0, smem2);              // 1 to 4 blocks remain; kb0 is a multiple of 3
-  if (kb0 + 1 < nkb) MFMA_STEP_TAIL(kb0 + 1, smem1, smem0);
-  if (kb0 + 2 < nkb) MFMA_STEP_TAIL(kb0 + 2, smem2, smem1);
-  if (kb0 + 3 < nkb) MFMA_STEP_TAIL(kb0 + 3, smem0, smem2);
+  if (partial) MFMA_KLOOP(true) else MFMA_KLOOP(false)
+#undef MFMA_KLOOP
 #undef MFMA_STEP_TAIL
 #undef MFMA_STEP
 #undef MFMA_ISSUE

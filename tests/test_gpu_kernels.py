@@ -222,7 +222,8 @@ def _gemm_case(seed, M_groups, N, K, gather_rows=None):
 
 
 # Group sizes pick the kernel: <= 16 rows on average the weight-streaming kernel, else the LDS
-# tile kernel with 32-, 64- or 128-row tiles.
+# tile kernel with 32-, 64- or 128-row tiles; a group's partial last tile runs the kernel's
+# partial-tile path (row blocks past the group's end skipped).
 GEMM_CASES = [
     ([16], 128, 128, None),
     ([1, 0, 37, 5, 130, 0, 64], 256, 384, None),
@@ -231,6 +232,8 @@ GEMM_CASES = [
     ([3] * 40, 256, 256, 50),
     ([100, 0, 129, 255, 7, 160], 384, 640, None),   # 128-row tiles: partial column tile, K tail of 2
     ([70, 90], 256, 128, 60),                        # 128-row tiles, one K block
+    ([130, 0, 161, 95, 170, 224], 384, 640, None),   # partial second tiles of 2, 33, 42 and 96 rows
+    ([150, 120, 118], 512, 256, 200),                # gathered rows, partial tiles of 22..120 rows, two K blocks
 ]
 
 
@@ -247,7 +250,7 @@ def test_grouped_gemm_store_f32(case):
     assert np.all(np.abs(got - ref) <= FP8_MFMA_REL * _absdot(a_q, a_s, gat, b_q, b_s, off) + 1e-30)
 
 
-@pytest.mark.parametrize("mg", [[5, 0, 70, 33], [70, 100, 0, 90]])
+@pytest.mark.parametrize("mg", [[5, 0, 70, 33], [70, 100, 0, 90], [150, 0, 170, 200]])
 def test_grouped_gemm_bf16_and_scatter(mg):
     say(f"grouped GEMM bf16 + weighted scatter-add groups={mg}")
     N, K = 256, 256
@@ -273,7 +276,8 @@ def test_grouped_gemm_bf16_and_scatter(mg):
 
 @pytest.mark.parametrize("mg,W,K,wide", [([7, 0, 130], 128, 256, False), ([64] * 5, 256, 512, False),
                                          ([1000], 128, 384, False), ([40, 90], 128, 256, True),
-                                         ([130, 0, 75, 200], 256, 768, False), ([66, 128], 128, 128, False)])
+                                         ([130, 0, 75, 200], 256, 768, False), ([66, 128], 128, 128, False),
+                                         ([140, 0, 200, 161], 256, 768, False), ([120, 130], 128, 128, False)])
 def test_grouped_gemm_swiglu_quant(mg, W, K, wide):
     say(f"grouped GEMM SwiGLU+quant groups={mg} W={W} K={K} full-range codes={wide}")
     a_q, a_s, b_q, b_s, off, _ = _gemm_case(W + K, mg, 2 * W, K)
