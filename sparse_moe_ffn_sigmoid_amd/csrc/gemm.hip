@@ -210,6 +210,7 @@ template <int NB, int NTW, int P, int EPI>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   constexpr int NF = NB * NTW;                 // B fragments per lane per K block
   constexpr int CW = 16 * NTW;                 // columns per wave in each B block
+  static_assert(EPI != kEpiSwiglu || NTW % 2 == 0, "the SwiGLU epilogue encodes h in pairs");
   constexpr bool kExact = EPI == kEpiSwiglu;
   __shared__ float red[4][16];
   __shared__ __attribute__((aligned(16))) uint8_t stage[16 * 128];
@@ -346,8 +347,13 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
       const int r = 4 * q + i;
       const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
       const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
+      const float inv = 1.0f / sc;                // x * inv is within an ulp of x / sc (equal for power-of-two sc)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) stage[r * 128 + wave * CW + 16 * j + r16] = (uint8_t)e4m3_encode(h[j][i] / sc);
+      for (int j = 0; j < NTW; j += 2) {
+        const uint32_t c2 = e4m3_encode2(h[j][i] * inv, h[j + 1][i] * inv);
+        stage[r * 128 + wave * CW + 16 * j + r16] = (uint8_t)c2;
+        stage[r * 128 + wave * CW + 16 * (j + 1) + r16] = (uint8_t)(c2 >> 8);
+      }
       if (wave == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + (nbase >> 7)] = sc;
     }
     __syncthreads();
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   constexpr int kLoads = A_LOADS + B_LOADS + 1; // + one scale load
   static_assert(A_LOADS * NW == BM / 8 && B_LOADS * NW == 32, "loads must split evenly over the waves");
   static_assert(BM / 32 <= NW && BM % 32 == 0, "one scale load per wave at most");
-  static_assert(!kExact || NTW % 2 == 0, "SwiGLU waves hold gate and up tiles in pairs");
+  static_assert(!kExact || NTW % 4 == 0, "SwiGLU waves hold gate and up tiles in pairs and encode h in pairs");
   // one array per pipeline stage: the compiler can then tell the stages apart and does
   // not wait for every LDS-DMA load before each LDS read
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
@@ -715,9 +721,13 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 #pragma unroll
         for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[w2][r]);
         const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
+        const float inv = 1.0f / sc;              // x * inv is within an ulp of x / sc (equal for power-of-two sc)
 #pragma unroll
-        for (int j = 0; j < H; ++j)
-          stage[r * 128 + wn * 16 * H + 16 * j + r16] = (uint8_t)e4m3_encode(h[mi][j][i] / sc);
+        for (int j = 0; j < H; j += 2) {
+          const uint32_t c2 = e4m3_encode2(h[mi][j][i] * inv, h[mi][j + 1][i] * inv);
+          stage[r * 128 + wn * 16 * H + 16 * j + r16] = (uint8_t)c2;
+          stage[r * 128 + wn * 16 * H + 16 * (j + 1) + r16] = (uint8_t)(c2 >> 8);
+        }
         if (wn == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + nt] = sc;
       }
     __syncthreads();
