@@ -645,7 +645,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   // them apart and keeps the other stages' loads in flight.  The main loop has no branches
   // inside: with control flow in the loop body the compiler's wait insertion loses track of
   // which stage a pending LDS-DMA load writes and waits for all of them before LDS reads.
-  // The last one to four blocks run in a peeled tail with the bounds checks.
+  // The last one to four blocks run in a peeled tail.
 #define MFMA_STEP(kb_, cur_, nxt_, skip_)                                                             \
   {                                                                                                   \
     wait_vmcnt<kLoads>();                                                                             \
@@ -653,7 +653,18 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
     MFMA_ISSUE((kb_) + 2, nxt_);                                                                      \
     if (wave_has_rows) compute((cur_) + lane_off, skip_);                                             \
   }
-#define MFMA_STEP_TAIL(kb_, cur_, nxt_, skip_)                                                        \
+// Step t of a tail of R steps (t, R literals: straight-line code, no branches for the compiler's
+// wait insertion to merge over): block kb0 + t, whose successor is in flight unless t + 1 == R.
+#define MFMA_STEP_TAIL(t_, R_, cur_, nxt_, skip_)                                                     \
+  {                                                                                                   \
+    if ((t_) + 1 < (R_)) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();                                  \
+    block_barrier();                                                                                  \
+    if ((t_) + 2 < (R_)) MFMA_ISSUE(kb0 + (t_) + 2, nxt_);                                            \
+    if (wave_has_rows) compute((cur_) + lane_off, skip_);                                             \
+  }
+// The same with run-time bounds checks (one copy of the tail: fewer registers, but the compiler then
+// waits for every LDS-DMA load, the just-issued ones included, before the step's LDS reads).
+#define MFMA_STEP_TAIL_RT(kb_, cur_, nxt_, skip_)                                                     \
   {                                                                                                   \
     const int kbs = (kb_);                                                                            \
     if (kbs + 1 < nkb) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();                                    \
@@ -672,14 +683,40 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
       MFMA_STEP(kb0 + 1, smem1, smem0, skip_);                                                        \
       MFMA_STEP(kb0 + 2, smem2, smem1, skip_);                                                        \
     }                                                                                                 \
-    MFMA_STEP_TAIL(kb0, smem0, smem2, skip_);  /* 1 to 4 blocks remain; kb0 is a multiple of 3 */     \
-    if (kb0 + 1 < nkb) MFMA_STEP_TAIL(kb0 + 1, smem1, smem0, skip_);                                  \
-    if (kb0 + 2 < nkb) MFMA_STEP_TAIL(kb0 + 2, smem2, smem1, skip_);                                  \
-    if (kb0 + 3 < nkb) MFMA_STEP_TAIL(kb0 + 3, smem0, smem2, skip_);                                  \
+    /* 2 to 4 blocks remain (1 when nkb == 1); kb0 is a multiple of 3.  The SwiGLU kernel, at its    \
+       register limit, and the 4-wave kernels keep the single run-time-checked copy (the gate/up      \
+       tail is 2 of 56 blocks at V3 shapes); the 8-wave plain kernels (the down GEMM's tail is 4 of   \
+       16) take the straight-line copies. */                                                          \
+    if constexpr (kExact || NW < 8) {                                                                 \
+      MFMA_STEP_TAIL_RT(kb0, smem0, smem2, skip_);                                                    \
+      if (kb0 + 1 < nkb) MFMA_STEP_TAIL_RT(kb0 + 1, smem1, smem0, skip_);                             \
+      if (kb0 + 2 < nkb) MFMA_STEP_TAIL_RT(kb0 + 2, smem2, smem1, skip_);                             \
+      if (kb0 + 3 < nkb) MFMA_STEP_TAIL_RT(kb0 + 3, smem0, smem2, skip_);                             \
+    } else switch (nkb - kb0) {                                                                       \
+      case 1:                                                                                         \
+        MFMA_STEP_TAIL(0, 1, smem0, smem2, skip_);                                                    \
+        break;                                                                                        \
+      case 2:                                                                                         \
+        MFMA_STEP_TAIL(0, 2, smem0, smem2, skip_);                                                    \
+        MFMA_STEP_TAIL(1, 2, smem1, smem0, skip_);                                                    \
+        break;                                                                                        \
+      case 3:                                                                                         \
+        MFMA_STEP_TAIL(0, 3, smem0, smem2, skip_);                                                    \
+        MFMA_STEP_TAIL(1, 3, smem1, smem0, skip_);                                                    \
+        MFMA_STEP_TAIL(2, 3, smem2, smem1, skip_);                                                    \
+        break;                                                                                        \
+      default:                                                                                        \
+        MFMA_STEP_TAIL(0, 4, smem0, smem2, skip_);                                                    \
+        MFMA_STEP_TAIL(1, 4, smem1, smem0, skip_);                                                    \
+        MFMA_STEP_TAIL(2, 4, smem2, smem1, skip_);                                                    \
+        MFMA_STEP_TAIL(3, 4, smem0, smem2, skip_);                                                    \
+        break;                                                                                        \
+    }                                                                                                 \
   }
 
   if (partial) MFMA_KLOOP(true) else MFMA_KLOOP(false)
 #undef MFMA_KLOOP
+#undef MFMA_STEP_TAIL_RT
 #undef MFMA_STEP_TAIL
 #undef MFMA_STEP
 #undef MFMA_ISSUE
