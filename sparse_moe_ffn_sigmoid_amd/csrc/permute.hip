@@ -199,6 +199,10 @@ __global__ __launch_bounds__(256) void perm_gather_kernel(const uint4* __restric
 }
 
 // out[t][c] = bf16(sum_j w[t][j] * y[assign_pos[t*k+j]][c] (+ shared[t][c])), fp32, slot order.
+// KT > 0: k fixed at compile time, so a thread has all its index loads, then all its row loads, in
+// flight together (two memory round trips); KT == 0: k at run time.  The sum is taken in the same
+// order either way.
+template <int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ ap,
                                                       const float* __restrict__ w, const float* __restrict__ shared,
                                                       int T, int k, int d, uint16_t* __restrict__ out) {
@@ -208,13 +212,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const long t = i / dv;
   const int c = (int)(i - t * dv) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + (long)ap[t * k + j] * d + c);
+  auto add = [&](float wj, const float4& v) {
     acc.x = fmaf(wj, v.x, acc.x);
     acc.y = fmaf(wj, v.y, acc.y);
     acc.z = fmaf(wj, v.z, acc.z);
     acc.w = fmaf(wj, v.w, acc.w);
+  };
+  if constexpr (KT > 0) {
+    int pos[KT];
+    float wv[KT];
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      pos[j] = ap[t * KT + j];
+      wv[j] = w[t * KT + j];
+    }
+    float4 v[KT];
+#pragma unroll
+    for (int j = 0; j < KT; ++j) v[j] = *reinterpret_cast<const float4*>(y + (long)pos[j] * d + c);
+#pragma unroll
+    for (int j = 0; j < KT; ++j) add(wv[j], v[j]);
+  } else {
+    for (int j = 0; j < k; ++j) add(w[t * k + j], *reinterpret_cast<const float4*>(y + (long)ap[t * k + j] * d + c));
   }
   if (shared) {
     const float4 v = *reinterpret_cast<const float4*>(shared + t * d + c);
@@ -292,7 +310,12 @@ hipError_t launch_combine(const float* y, const int32_t* ap, const float* w, con
                           uint16_t* out, hipStream_t st) {
   const long total = (long)T * (d / 4);
   if (total == 0) return hipSuccess;
-  combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(y, ap, w, shared, T, k, d, out);
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  switch (k) {
+    case 8: combine_kernel<8><<<grid, 256, 0, st>>>(y, ap, w, shared, T, k, d, out); break;
+    case 2: combine_kernel<2><<<grid, 256, 0, st>>>(y, ap, w, shared, T, k, d, out); break;
+    default: combine_kernel<0><<<grid, 256, 0, st>>>(y, ap, w, shared, T, k, d, out); break;
+  }
   return hipGetLastError();
 }
 
