@@ -187,8 +187,13 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& s
     locate_tile(sd, bm, scan, v / ny1, g, start, c);
     panel_map(v - ny1 * start, c, ny1, mt, nt);
     si = 1;
-    m0 = sd.offsets[g] + mt * bm;
-    m_end = sd.offsets[g + 1];
+    // a group's rows are split evenly over its c tiles, in whole 16-row blocks (150 rows: 80 + 70,
+    // not 128 + 22): the tiles of one n tile stream the same B tile however the rows fall, and
+    // two tiles of partial row blocks cost less than a full tile plus a nearly empty one
+    const int off = sd.offsets[g], end = sd.offsets[g + 1];
+    const int rb = c > 1 ? ((end - off + c - 1) / c + 15) & ~15 : bm;
+    m0 = off + mt * rb;
+    m_end = min(m0 + rb, end);
   }
   nt = __builtin_amdgcn_readfirstlane(nt);
   m0 = __builtin_amdgcn_readfirstlane(m0);
