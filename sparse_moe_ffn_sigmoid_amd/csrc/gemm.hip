@@ -164,25 +164,31 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& s
                           int& nt) {
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& sd = args.seg[1];
-  const int w0 = s0.m_tiles * ny0;
-  GroupTiles scan{0, 0, 0};
-  if (sd.m_tiles > 0) scan = scan_group_tiles(sd, bm);
-  const int c1 = scan.total;
-  const int total = w0 + c1 * ny1;
-  const int chunk = (total + 7) >> 3;
-  const int b = blockIdx.x, j = b >> 3;
-  if (j >= chunk) return false;
-  const int w = (b & 7) * chunk + j;
-  if (w >= total) return false;
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;   // XCD, position in its sequence
+  // static segment: panel p goes to XCD p % 8; this XCD's panels come first in its sequence
+  const int panels = (s0.m_tiles + kPanel - 1) / kPanel, per_panel = kPanel * ny0;
+  const int mine = panels > x ? (panels - 1 - x) / 8 + 1 : 0;
+  const int last_m = s0.m_tiles - (panels - 1) * kPanel;   // m tiles of the last panel
+  const int s_items = mine == 0 ? 0 : (mine - 1) * per_panel + ((x + 8 * (mine - 1)) == panels - 1 ? last_m * ny0 : per_panel);
   int mt;
-  if (w < w0) {
-    panel_map(w, s0.m_tiles, ny0, mt, nt);
+  if (j < s_items) {
+    const int kp = j / per_panel, L = j - kp * per_panel, p = x + 8 * kp;
+    const int c = p == panels - 1 ? last_m : kPanel;
+    nt = L / c;
+    mt = p * kPanel + (L - nt * c);
     si = 0;
     g = 0;
     m0 = mt * bm;
     m_end = s0.m_rows;
   } else {
-    const int v = w - w0;
+    // dynamic segment: 8 equal contiguous chunks, chunk x after this XCD's static panels
+    GroupTiles scan{0, 0, 0};
+    if (sd.m_tiles > 0) scan = scan_group_tiles(sd, bm);
+    const int dyn = scan.total * ny1, chunk = (dyn + 7) >> 3;
+    const int dj = j - s_items;
+    if (dj >= chunk) return false;
+    const int v = x * chunk + dj;
+    if (v >= dyn) return false;
     int start, c;
     locate_tile(sd, bm, scan, v / ny1, g, start, c);
     panel_map(v - ny1 * start, c, ny1, mt, nt);
@@ -568,14 +574,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 #pragma unroll
     for (int f = 0; f < NTW; ++f) acc[mi][f] = v4f{0.f, 0.f, 0.f, 0.f};
   const int lane_off = lane * 16;
-  // In a partial tile a wave computes only its 16-row blocks that hold rows of the group (uniform
-  // branches between row blocks; full tiles run a copy of the K loop without them), and a wave
-  // with none of them only loads and synchronises.
+  // In a partial tile a wave computes only its 16-row blocks that hold rows of the group (nmi of
+  // them, from its own copy of the K loop below), and a wave with none of them only loads and
+  // synchronises.
   const int nmi = __builtin_amdgcn_readfirstlane(min(MT, max(0, (m_end - m0 - wm * 16 * MT + 15) / 16)));
   const bool wave_has_rows = nmi > 0;
 
   // MFMAs and scale promotion of one K block from the LDS stage at st (+ this lane's offset)
-  auto compute = [&](const uint8_t* st, bool skip) __attribute__((always_inline)) {
+  auto compute = [&](const uint8_t* st, int nblk) __attribute__((always_inline)) {
     const uint8_t* const stb = st - lane_off;
     auto load_a = [&](int mi) {
       const int ab = wm * MT + mi;
@@ -602,7 +608,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
     }
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
-      if (skip && mi > 0 && mi >= nmi) break;   // the wave's remaining row blocks lie past the group's end
+      if (mi >= nblk) break;                    // row blocks past the group's end (nblk: a constant per copy)
       const int ab = wm * MT + mi;
       const v8i af = af_next;
       if (mi + 1 < MT) af_next = load_a(mi + 1);
@@ -651,76 +657,132 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   // inside: with control flow in the loop body the compiler's wait insertion loses track of
   // which stage a pending LDS-DMA load writes and waits for all of them before LDS reads.
   // The last one to four blocks run in a peeled tail.
-#define MFMA_STEP(kb_, cur_, nxt_, skip_)                                                             \
+#define MFMA_STEP(kb_, cur_, nxt_, nblk_)                                                             \
   {                                                                                                   \
     wait_vmcnt<kLoads>();                                                                             \
     block_barrier();                                                                                  \
     MFMA_ISSUE((kb_) + 2, nxt_);                                                                      \
-    if (wave_has_rows) compute((cur_) + lane_off, skip_);                                             \
+    if (wave_has_rows) compute((cur_) + lane_off, nblk_);                                             \
   }
 // Step t of a tail of R steps (t, R literals: straight-line code, no branches for the compiler's
 // wait insertion to merge over): block kb0 + t, whose successor is in flight unless t + 1 == R.
-#define MFMA_STEP_TAIL(t_, R_, cur_, nxt_, skip_)                                                     \
+#define MFMA_STEP_TAIL(t_, R_, cur_, nxt_, nblk_)                                                     \
   {                                                                                                   \
     if ((t_) + 1 < (R_)) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();                                  \
     block_barrier();                                                                                  \
     if ((t_) + 2 < (R_)) MFMA_ISSUE(kb0 + (t_) + 2, nxt_);                                            \
-    if (wave_has_rows) compute((cur_) + lane_off, skip_);                                             \
+    if (wave_has_rows) compute((cur_) + lane_off, nblk_);                                             \
   }
 // The same with run-time bounds checks (one copy of the tail: fewer registers, but the compiler then
 // waits for every LDS-DMA load, the just-issued ones included, before the step's LDS reads).
-#define MFMA_STEP_TAIL_RT(kb_, cur_, nxt_, skip_)                                                     \
+#define MFMA_STEP_TAIL_RT(kb_, cur_, nxt_, nblk_)                                                     \
   {                                                                                                   \
     const int kbs = (kb_);                                                                            \
     if (kbs + 1 < nkb) wait_vmcnt<kLoads>(); else wait_vmcnt<0>();                                    \
     block_barrier();                                                                                  \
     if (kbs + 2 < nkb) MFMA_ISSUE(kbs + 2, nxt_);                                                     \
-    if (wave_has_rows) compute((cur_) + lane_off, skip_);                                             \
+    if (wave_has_rows) compute((cur_) + lane_off, nblk_);                                             \
   }
-#define MFMA_KLOOP(skip_)                                                                             \
+// K loop without a tail (partial tiles of the SwiGLU kernel): whole rounds of 3 steps; a step past
+// the last block issues a surplus copy of the last block (an unconditional issue keeps the
+// compiler's tracking of the stages intact) and computes nothing; the surplus loads land before
+// the stages are reused.
+#define MFMA_STEP_PAD(kb_, cur_, nxt_, nblk_)                                                         \
+  {                                                                                                   \
+    const int kbs = (kb_);                                                                            \
+    wait_vmcnt<kLoads>();                                                                             \
+    block_barrier();                                                                                  \
+    MFMA_ISSUE(min(kbs + 2, nkb - 1), nxt_);                                                          \
+    if (wave_has_rows && kbs < nkb) compute((cur_) + lane_off, nblk_);                                \
+  }
+#define MFMA_KLOOP_PAD(nblk_)                                                                         \
+  {                                                                                                   \
+    MFMA_ISSUE(0, smem0);                                                                             \
+    MFMA_ISSUE(nkb > 1 ? 1 : 0, smem1);                                                               \
+    for (int kb0 = 0; kb0 < nkb; kb0 += 3) {                                                          \
+      MFMA_STEP_PAD(kb0, smem0, smem2, nblk_);                                                        \
+      MFMA_STEP_PAD(kb0 + 1, smem1, smem0, nblk_);                                                    \
+      MFMA_STEP_PAD(kb0 + 2, smem2, smem1, nblk_);                                                    \
+    }                                                                                                 \
+    wait_vmcnt<0>();                                                                                  \
+  }
+// K loop with a peeled tail (nkb steps).
+#define MFMA_KLOOP(nblk_)                                                                             \
   {                                                                                                   \
     MFMA_ISSUE(0, smem0);                                                                             \
     MFMA_ISSUE(nkb > 1 ? 1 : 0, smem1);  /* unconditional (no branch before the loop); for nkb == 1  \
                                             a copy of block 0 that is never read */                   \
     int kb0 = 0;                                                                                      \
     for (; kb0 + 4 < nkb; kb0 += 3) {    /* every step here issues block kb + 2 < nkb */              \
-      MFMA_STEP(kb0, smem0, smem2, skip_);                                                            \
-      MFMA_STEP(kb0 + 1, smem1, smem0, skip_);                                                        \
-      MFMA_STEP(kb0 + 2, smem2, smem1, skip_);                                                        \
+      MFMA_STEP(kb0, smem0, smem2, nblk_);                                                            \
+      MFMA_STEP(kb0 + 1, smem1, smem0, nblk_);                                                        \
+      MFMA_STEP(kb0 + 2, smem2, smem1, nblk_);                                                        \
     }                                                                                                 \
-    /* 2 to 4 blocks remain (1 when nkb == 1); kb0 is a multiple of 3.  The SwiGLU kernel, at its    \
-       register limit, and the 4-wave kernels keep the single run-time-checked copy (the gate/up      \
-       tail is 2 of 56 blocks at V3 shapes); the 8-wave plain kernels (the down GEMM's tail is 4 of   \
-       16) take the straight-line copies. */                                                          \
+    /* 2 to 4 blocks remain (1 when nkb == 1); kb0 is a multiple of 3.  The SwiGLU and 4-wave       \
+       kernels keep the single run-time-checked copy (the straight-line ones push them past their     \
+       register budget); the 8-wave plain kernels (the down GEMM's tail is 4 of 16 blocks) take the   \
+       straight-line copies. */                                                                       \
     if constexpr (kExact || NW < 8) {                                                                 \
-      MFMA_STEP_TAIL_RT(kb0, smem0, smem2, skip_);                                                    \
-      if (kb0 + 1 < nkb) MFMA_STEP_TAIL_RT(kb0 + 1, smem1, smem0, skip_);                             \
-      if (kb0 + 2 < nkb) MFMA_STEP_TAIL_RT(kb0 + 2, smem2, smem1, skip_);                             \
-      if (kb0 + 3 < nkb) MFMA_STEP_TAIL_RT(kb0 + 3, smem0, smem2, skip_);                             \
+      MFMA_STEP_TAIL_RT(kb0, smem0, smem2, nblk_);                                                    \
+      if (kb0 + 1 < nkb) MFMA_STEP_TAIL_RT(kb0 + 1, smem1, smem0, nblk_);                             \
+      if (kb0 + 2 < nkb) MFMA_STEP_TAIL_RT(kb0 + 2, smem2, smem1, nblk_);                             \
+      if (kb0 + 3 < nkb) MFMA_STEP_TAIL_RT(kb0 + 3, smem0, smem2, nblk_);                             \
     } else switch (nkb - kb0) {                                                                       \
       case 1:                                                                                         \
-        MFMA_STEP_TAIL(0, 1, smem0, smem2, skip_);                                                    \
+        MFMA_STEP_TAIL(0, 1, smem0, smem2, nblk_);                                                    \
         break;                                                                                        \
       case 2:                                                                                         \
-        MFMA_STEP_TAIL(0, 2, smem0, smem2, skip_);                                                    \
-        MFMA_STEP_TAIL(1, 2, smem1, smem0, skip_);                                                    \
+        MFMA_STEP_TAIL(0, 2, smem0, smem2, nblk_);                                                    \
+        MFMA_STEP_TAIL(1, 2, smem1, smem0, nblk_);                                                    \
         break;                                                                                        \
       case 3:                                                                                         \
-        MFMA_STEP_TAIL(0, 3, smem0, smem2, skip_);                                                    \
-        MFMA_STEP_TAIL(1, 3, smem1, smem0, skip_);                                                    \
-        MFMA_STEP_TAIL(2, 3, smem2, smem1, skip_);                                                    \
+        MFMA_STEP_TAIL(0, 3, smem0, smem2, nblk_);                                                    \
+        MFMA_STEP_TAIL(1, 3, smem1, smem0, nblk_);                                                    \
+        MFMA_STEP_TAIL(2, 3, smem2, smem1, nblk_);                                                    \
         break;                                                                                        \
       default:                                                                                        \
-        MFMA_STEP_TAIL(0, 4, smem0, smem2, skip_);                                                    \
-        MFMA_STEP_TAIL(1, 4, smem1, smem0, skip_);                                                    \
-        MFMA_STEP_TAIL(2, 4, smem2, smem1, skip_);                                                    \
-        MFMA_STEP_TAIL(3, 4, smem0, smem2, skip_);                                                    \
+        MFMA_STEP_TAIL(0, 4, smem0, smem2, nblk_);                                                    \
+        MFMA_STEP_TAIL(1, 4, smem1, smem0, nblk_);                                                    \
+        MFMA_STEP_TAIL(2, 4, smem2, smem1, nblk_);                                                    \
+        MFMA_STEP_TAIL(3, 4, smem0, smem2, nblk_);                                                    \
         break;                                                                                        \
     }                                                                                                 \
   }
 
-  if (partial) MFMA_KLOOP(true) else MFMA_KLOOP(false)
+  // One branch-free copy of the K loop per count of row blocks a wave computes (a branch per row
+  // block made the compiler's wait insertion lose track of the LDS-DMA stages and wait for every
+  // load once per unrolled iteration); a wave without rows runs the 1-block copy, compute off.  The
+  // waves of a workgroup may run different copies, so every copy a workgroup can choose must pass
+  // the same barriers: the loop form is chosen per tile.  SwiGLU kernel: full tiles run the loop
+  // with the checked tail (nkb steps); partial tiles run padded copies (whole rounds of 3 steps),
+  // since next to the checked tail any further copy of that loop again waited for every load.
+  // Plain kernels: every copy has the straight-line tail.
+  {
+    const int nk = nmi < 1 ? 1 : nmi;
+    if constexpr (kExact) {
+      if (!partial) MFMA_KLOOP(MT)
+      else if (nk >= MT) MFMA_KLOOP_PAD(MT)
+      else if constexpr (MT == 4) {
+        if (nk == 3) MFMA_KLOOP_PAD(3)
+        else if (nk == 2) MFMA_KLOOP_PAD(2)
+        else MFMA_KLOOP_PAD(1)
+      } else if constexpr (MT == 2) {
+        MFMA_KLOOP_PAD(1)
+      }
+    } else {
+      if (nk >= MT) MFMA_KLOOP(MT)
+      else if constexpr (MT == 4) {
+        if (nk == 3) MFMA_KLOOP(3)
+        else if (nk == 2) MFMA_KLOOP(2)
+        else MFMA_KLOOP(1)
+      } else if constexpr (MT == 2) {
+        MFMA_KLOOP(1)
+      }
+    }
+  }
 #undef MFMA_KLOOP
+#undef MFMA_KLOOP_PAD
+#undef MFMA_STEP_PAD
 #undef MFMA_STEP_TAIL_RT
 #undef MFMA_STEP_TAIL
 #undef MFMA_STEP
@@ -822,13 +884,16 @@ static void launch_mfma_cfg(const GemmArgs& args, dim3 grid, hipStream_t st) {
 template <int MT>
 static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
   const bool swiglu = epi == kEpiSwiglu;
-  long items = 0;                               // upper bound of the work items (m tiles reserved x n tiles)
-  for (int s = 0; s < 2; ++s) {
-    const GemmSeg& S = args.seg[s];
-    if (S.m_tiles > 0) items += (long)S.m_tiles * (swiglu ? S.N / 256 : (S.N + 255) / 256);
-  }
-  if (items == 0) return hipSuccess;
-  const dim3 grid((unsigned)(8 * ((items + 7) / 8)));   // whole rounds over the 8 XCDs
+  // workgroups per XCD: its static panels (at most ceil(panels / 8) of them) and an eighth of the
+  // dynamic segment's items (upper bound: m tiles reserved x n tiles)
+  const GemmSeg& S0 = args.seg[0];
+  const GemmSeg& S1 = args.seg[1];
+  const long ny0 = S0.m_tiles > 0 ? (swiglu ? S0.N / 256 : (S0.N + 255) / 256) : 0;
+  const long ny1 = S1.m_tiles > 0 ? (swiglu ? S1.N / 256 : (S1.N + 255) / 256) : 0;
+  const long panels = ((long)S0.m_tiles + kPanel - 1) / kPanel;
+  const long per_xcd = (panels + 7) / 8 * kPanel * ny0 + ((long)S1.m_tiles * ny1 + 7) / 8;
+  if (per_xcd == 0) return hipSuccess;
+  const dim3 grid((unsigned)(8 * per_xcd));
   switch (epi) {
     case kEpiSwiglu:
       if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiSwiglu>(args, grid, st);
