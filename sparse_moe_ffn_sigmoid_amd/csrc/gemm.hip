@@ -40,9 +40,10 @@
 
 namespace moefp8 {
 
-// Tiles of the dynamic segment: group g has ceil(rows_g / bm) tiles of bm rows.  Each wave
-// scans the per-group counts on its own, with cross-lane shuffles (no LDS, no barrier; every
-// wave of a workgroup gets the same result): lane l owns groups l * per .. l * per + per - 1.
+// Tiles of the dynamic segment: group g has ceil(rows_g / bm) tiles (its rows split evenly over
+// them by the tile kernel, in whole 16-row blocks).  Each wave scans the per-group counts on its
+// own, with cross-lane shuffles (no LDS, no barrier; every wave of a workgroup gets the same
+// result): lane l owns groups l * per .. l * per + per - 1.
 struct GroupTiles {
   int per;        // groups per lane (G <= 1024)
   int first;      // this lane's first tile: the tiles of all groups of the lanes below it
@@ -435,7 +436,9 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
 // chunk index XORed by (row & 7), which keeps the 16 lanes of a ds_read_b128
 // phase on distinct banks.  3 LDS stages, one barrier per K block.  Per K block
 // each wave issues the same number of loads (kLoads), so "my loads for block
-// kb are done" is a constant vmcnt.
+// kb are done" is a constant vmcnt.  Tiles with fewer rows than BM (a group's
+// last, or all of a small group's) compute only their row blocks, from copies
+// of the K loop compiled per count of active row blocks (see the kernel).
 constexpr int kStages = 3;
 
 __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base) {
