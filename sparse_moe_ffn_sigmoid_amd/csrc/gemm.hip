@@ -457,6 +457,15 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier after this wave's LDS accesses have completed (lgkmcnt(0)), without the wait
+// for every outstanding global load and store that __syncthreads() adds.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);           // vmcnt 63 and expcnt 7: no wait; lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14];
 // expcnt and lgkmcnt left at their "no wait" maxima).
 template <int N>
@@ -478,6 +487,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   constexpr int kLoads = A_LOADS + B_LOADS + 1; // + one scale load
   static_assert(A_LOADS * NW == BM / 8 && B_LOADS * NW == 32, "loads must split evenly over the waves");
   static_assert(BM / 32 <= NW && BM % 32 == 0, "one scale load per wave at most");
+  static_assert(!kExact || (WN >= 2 && BM <= 64 * NW), "the SwiGLU epilogue's per-row scales: red[0..1], a thread per row");
   static_assert(!kExact || NTW % 4 == 0, "SwiGLU waves hold gate and up tiles in pairs and encode h in pairs");
   // one array per pipeline stage: the compiler can then tell the stages apart and does
   // not wait for every LDS-DMA load before each LDS read
@@ -818,24 +828,32 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
         if (r16 == 0) red[wn][wm * 16 * MT + mi * 16 + 4 * q + i] = mx;
       }
     __syncthreads();                                // also: every wave is past its last LDS stage read
+    // one thread per row: the tile's amax, its scale and the scale's reciprocal (red[0][r] and
+    // red[1][r] then hold sc and 1/sc; only this thread reads row r's partial maxima)
+    if (tid < BM) {
+      const int r = tid;
+      float amax = red[0][r];
+#pragma unroll
+      for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[w2][r]);
+      const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
+      red[0][r] = sc;
+      red[1][r] = 1.0f / sc;                        // x * (1/sc) is within an ulp of x / sc (equal for power-of-two sc)
+      if (m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + nt] = sc;
+    }
+    lds_barrier();
     uint8_t* stage = smem0;                         // BM x 128 codes
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wm * 16 * MT + mi * 16 + 4 * q + i;
-        float amax = red[0][r];
-#pragma unroll
-        for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[w2][r]);
-        const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
-        const float inv = 1.0f / sc;              // x * inv is within an ulp of x / sc (equal for power-of-two sc)
+        const float inv = red[1][r];
 #pragma unroll
         for (int j = 0; j < H; j += 2) {
           const uint32_t c2 = e4m3_encode2(h[mi][j][i] * inv, h[mi][j + 1][i] * inv);
           stage[r * 128 + wn * 16 * H + 16 * j + r16] = (uint8_t)c2;
           stage[r * 128 + wn * 16 * H + 16 * (j + 1) + r16] = (uint8_t)(c2 >> 8);
         }
-        if (wn == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + nt] = sc;
       }
     __syncthreads();
     for (int ci = tid; ci < BM * 8; ci += 64 * NW) {
