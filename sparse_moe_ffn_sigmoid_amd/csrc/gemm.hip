@@ -403,7 +403,7 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
   const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
   if (mt == 0) return hipSuccess;
   const bool swiglu = epi == kEpiSwiglu;
-  const int cols = swiglu ? 4 * 16 * 2 : 4 * 16 * 4;         // columns per workgroup in each block
+  const int cols = 4 * 16 * 2;                               // columns per workgroup in each block
   int ny = 0;
   for (int s = 0; s < 2; ++s) {
     const GemmSeg& S = args.seg[s];
@@ -416,10 +416,10 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
   if (ny == 0) return hipSuccess;
   const dim3 grid(mt, ny);
   switch (epi) {
-    case kEpiSwiglu: stream_gemm_kernel<2, 2, 4, kEpiSwiglu><<<grid, 256, 0, st>>>(args); break;
-    case kEpiF32: stream_gemm_kernel<1, 4, 4, kEpiF32><<<grid, 256, 0, st>>>(args); break;
-    case kEpiBf16: stream_gemm_kernel<1, 4, 4, kEpiBf16><<<grid, 256, 0, st>>>(args); break;
-    default: stream_gemm_kernel<1, 4, 4, kEpiScatter><<<grid, 256, 0, st>>>(args); break;
+    case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu><<<grid, 256, 0, st>>>(args); break;
+    case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32><<<grid, 256, 0, st>>>(args); break;
+    case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16><<<grid, 256, 0, st>>>(args); break;
+    default: stream_gemm_kernel<1, 2, 4, kEpiScatter><<<grid, 256, 0, st>>>(args); break;
   }
   return hipGetLastError();
 }
