@@ -137,7 +137,7 @@ def gate_up_kernel(shape) -> str:
     with 64 rows per wave for groups above 64 rows)."""
     rows = shape.tokens * shape.top_k / shape.n_experts if shape.n_experts else shape.tokens
     if rows <= 16:
-        return "stream_gemm_kernel<2, 2, 4, 2>"
+        return "stream_gemm_kernel<2, 2, 6, 2>"
     mt = 1 if rows <= 32 else 2 if rows <= 64 else 4
     return f"mfma_gemm_kernel<2, {4 if mt >= 2 else 2}, {mt}, 2>"
 
