@@ -263,7 +263,9 @@ MOE_API int moe_ffn_forward(const uint16_t* x, int T, const moe_cfg_t* cfg, cons
  *   events[0] before quantising x, [1] after it, [2] after routing and the
  *   permutation, [3] after the gate/up GEMM, [4] after the down GEMM,
  *   [5] after the combine/cast.
- * n_events must be 0 (then it is moe_ffn_forward) or MOE_FWD_STAGE_EVENTS.  */
+ * n_events must be 0 (then it is moe_ffn_forward) or MOE_FWD_STAGE_EVENTS; a
+ * NULL entry is not recorded (each record costs the stream a few
+ * microseconds, so a caller can time one stage alone).  */
 #define MOE_FWD_STAGE_EVENTS 6
 MOE_API int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
                                    size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w,
