@@ -62,6 +62,38 @@ def test_tiny_deterministic_repeat(tiny):
     assert np.array_equal(a["out"], b["out"])
 
 
+def test_forward_stages_events_optional(tiny):
+    """moe_ffn_forward_stages with every stage event, with NULL entries (not recorded) and with
+    none gives moe_ffn_forward's output bit for bit; the recorded events come in stage order."""
+    import ctypes
+    from sparse_moe_ffn_sigmoid_amd import _lib
+    say("forward_stages with all, some and no stage events")
+    xb = synth.gen_x(synth.TINY)
+    ref = _run(tiny, xb)["out"]
+    x = to_dev(xb)
+    T = x.shape[0]
+    ws = moe.alloc_workspace(T, tiny.cfg, DEV)
+    lib = _lib.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    c, wc = tiny.cfg.c(), tiny.weights.c()
+    n_ev = _lib.MOE_FWD_STAGE_EVENTS
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in evs:
+        e.record()                                # creates the event; the library records it again
+    torch.cuda.synchronize()
+    for keep in (tuple(range(n_ev)), (2, 3), ()):
+        out = torch.empty_like(x)
+        arr = (ctypes.c_void_p * n_ev)(*[evs[j].cuda_event if j in keep else None for j in range(n_ev)])
+        st = lib.moe_ffn_forward_stages(ctypes.c_void_p(x.data_ptr()), T, ctypes.byref(c), ctypes.byref(wc),
+                                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(out.data_ptr()),
+                                        None, None, None, 0, arr, n_ev, stream)
+        assert st == 0, lib.moe_last_error().decode()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_np(out), ref)
+        for a, b in zip(keep, keep[1:]):
+            assert evs[a].elapsed_time(evs[b]) >= 0.0
+
+
 def test_large_batch_is_bit_reproducible():
     """The combine is slot-ordered at every batch size: repeated runs agree bit for bit."""
     say("forward mid_large twice: bit-reproducible")
