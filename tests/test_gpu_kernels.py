@@ -234,6 +234,7 @@ GEMM_CASES = [
     ([70, 90], 256, 128, 60),                        # 128-row tiles, one K block
     ([130, 0, 161, 95, 170, 224], 384, 640, None),   # partial second tiles of 2, 33, 42 and 96 rows
     ([150, 120, 118], 512, 256, 200),                # gathered rows, partial tiles of 22..120 rows, two K blocks
+    ([3, 9, 0, 14, 1], 384, 256, 40),                # weight-streaming path: three 128-column workgroups
 ]
 
 
@@ -277,7 +278,8 @@ def test_grouped_gemm_bf16_and_scatter(mg):
 @pytest.mark.parametrize("mg,W,K,wide", [([7, 0, 130], 128, 256, False), ([64] * 5, 256, 512, False),
                                          ([1000], 128, 384, False), ([40, 90], 128, 256, True),
                                          ([130, 0, 75, 200], 256, 768, False), ([66, 128], 128, 128, False),
-                                         ([140, 0, 200, 161], 256, 768, False), ([120, 130], 128, 128, False)])
+                                         ([140, 0, 200, 161], 256, 768, False), ([120, 130], 128, 128, False),
+                                         ([5, 0, 12, 16, 3], 384, 256, False)])
 def test_grouped_gemm_swiglu_quant(mg, W, K, wide):
     say(f"grouped GEMM SwiGLU+quant groups={mg} W={W} K={K} full-range codes={wide}")
     a_q, a_s, b_q, b_s, off, _ = _gemm_case(W + K, mg, 2 * W, K)
