@@ -251,7 +251,7 @@ def test_grouped_gemm_store_f32(case):
     assert np.all(np.abs(got - ref) <= FP8_MFMA_REL * _absdot(a_q, a_s, gat, b_q, b_s, off) + 1e-30)
 
 
-@pytest.mark.parametrize("mg", [[5, 0, 70, 33], [70, 100, 0, 90], [150, 0, 170, 200]])
+@pytest.mark.parametrize("mg", [[3, 0, 9, 14], [5, 0, 70, 33], [70, 100, 0, 90], [150, 0, 170, 200]])
 def test_grouped_gemm_bf16_and_scatter(mg):
     say(f"grouped GEMM bf16 + weighted scatter-add groups={mg}")
     N, K = 256, 256
