@@ -29,6 +29,7 @@ MID_B = synth.MoeShape("mid_b", 11, 1024, 384, 256, 16, 4, 1, 384, 4, 4)
 MID_LARGE = synth.MoeShape("mid_large", 12, 2304, 256, 128, 16, 4, 1, 128, 4, 2)   # 9216 assignments
 NO_SHARED = synth.MoeShape("no_shared", 13, 100, 256, 128, 16, 2, 0, 0, 4, 2)
 DENSE_SMALL = synth.MoeShape("dense_small", 14, 300, 512, 0, 0, 0, 1, 640, 1, 1)
+MID_C = synth.MoeShape("mid_c", 15, 384, 256, 128, 64, 6, 1, 256, 8, 4)          # 36 rows per expert: 64-row tiles
 
 
 @pytest.fixture(scope="module")
@@ -103,7 +104,7 @@ def test_large_batch_is_bit_reproducible():
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["topk_idx"], b["topk_idx"])
 
 
-@pytest.mark.parametrize("shape", [MID_A, MID_B, MID_LARGE, NO_SHARED, DENSE_SMALL])
+@pytest.mark.parametrize("shape", [MID_A, MID_B, MID_C, MID_LARGE, NO_SHARED, DENSE_SMALL])
 def test_mid_shapes(shape):
     say(f"forward {shape.name} T={shape.tokens} d={shape.hidden} E={shape.n_experts} k={shape.top_k}")
     layer = Layer(shape)
