@@ -11,7 +11,8 @@
  *               active, 1 shared), "Structural change" (shared expert always on),
  *               "Local Balanced Routing to Experts" (affinity gating, routing-only
  *               bias), FP8 headings "Fine granularity quantization", "More Mantissa
- *               bits of fp8", "Better Accumulation Precision", "Online Quantization".
+ *               bits of fp8", "Better Accumulation Precision", "Online Quantization",
+ *               "More customized data format and scaling factor".
  *   [aguasto]   aguasto, "DeepSeek-R1" record, "Quantization" (blockwise FP8).
  *
  * Conventions for every call:
@@ -130,7 +131,7 @@ MOE_API const char* moe_last_error(void);
  * quantization", "Online Quantization").  Per row, per 128 consecutive columns:
  * amax = max |v|; s = fp32(amax / 448) (correctly rounded; 1.0 for an all-zero
  * tile), or with MOE_SCALE_UE8M0 the power of two of MOE_SCALE_UE8M0 ([arch
- * blog] "More Mantissa bits of fp8": a customised scaling factor);
+ * blog] "More customized data format and scaling factor");
  * q = e4m3(fp32(v / s)) rounded to nearest even, saturating.
  *   x      [rows][ld_x] of x_dtype (MOE_DTYPE_BF16 or MOE_DTYPE_F32), cols used
  *   q      e4m3 [rows][ld_q]

@@ -11,9 +11,9 @@ section bodies are missing from the page, so the oracle takes this reading:
   correctly rounded fp32 division, q_i = E4M3(fp32(v_i / s)) with a correctly
   rounded fp32 division; an all-zero tile gets s = 1 and codes 0x00.
 
-Power-of-two ("UE8M0") variant ([arch blog] "More Mantissa bits of fp8": a
-customised data format and scaling factor; the section body is missing, so
-this is a reading): s is the smallest power of two with amax / s <= 448, i.e.
+Power-of-two ("UE8M0") variant ([arch blog] heading "More customized data
+format and scaling factor"; the section body is missing, so this is a
+reading): s is the smallest power of two with amax / s <= 448, i.e.
 s = 2^k, k = ceil(log2(amax / 448)) decided exactly, clamped to [-127, 127]
 (the range of an 8-bit biased exponent); v_i / s is then exact and only the
 E4M3 rounding remains.  All-zero tiles keep s = 1.

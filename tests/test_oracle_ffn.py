@@ -146,3 +146,53 @@ def test_fp8_fidelity_informational(tiny):
     rel = np.linalg.norm(r["out_f64"] - ref) / np.linalg.norm(ref)
     print(f"FP8 layer vs unquantised fp64: relative L2 {rel:.3e}")
     assert rel < 0.2
+
+
+def test_expert_forward_hand_computed_single_token():
+    """One token through one gated expert, worked out by hand on small-integer codes: two 128-wide
+    K blocks with different activation scales, a weight block with scale 1/2, the gate rows before
+    the up rows, silu(z) = z / (1 + e^-z), h rounded to fp32 and requantised 1x128, then the down
+    projection.  The expected numbers are written out below with plain Python arithmetic (no
+    matmul, no oracle helper), so a dropped term, a swapped gate/up half, a wrong scale or a
+    transposed operand anywhere in the chain shows up."""
+    from oracle.ffn import QuantExpert
+    f32 = np.float32
+    d, W = 256, 128
+    # x: tile 0 has amax 448 (s = 1), tile 1 amax 7 (s = 7/448 = 1/64): codes are the values / s
+    E4 = {448.0: 0x7E, 2.0: 0x40, -3.0: 0xC4, 1.0: 0x38, 32.0: 0x60}   # e4m3 bytes of these values
+    a_q = np.zeros((1, d), np.uint8)
+    a_q[0, 0], a_q[0, 1], a_q[0, 2], a_q[0, 3] = E4[448.0], E4[2.0], E4[-3.0], E4[1.0]
+    a_q[0, 128], a_q[0, 129] = E4[448.0], E4[32.0]                    # x = 7 and 0.5 at scale 1/64
+    a_s = np.array([[1.0, 1.0 / 64]], np.float32)
+    # W13 [2W, d]: gate block (rows 0..127) scale 1, up block (rows 128..255) scale 1/2
+    w13 = np.zeros((2 * W, d), np.uint8)
+    w13[0, 1], w13[0, 3], w13[0, 128], w13[0, 129] = E4[1.0], E4[1.0], E4[1.0], E4[2.0]   # g0 = 2+1+7+2*0.5 = 11
+    w13[1, 2] = E4[1.0]                                                                 # g1 = -3
+    w13[2, 0] = E4[1.0]                                                                 # g2 = 448
+    w13[127, 127] = w13[255, 255] = E4[448.0]                     # block amax (x is 0 there)
+    w13[W + 0, 1] = E4[2.0]                                       # u0 = 2 * (2 * 1/2) = 2
+    w13[W + 1, 3], w13[W + 1, 129] = E4[2.0], E4[32.0]            # u1 = 1*1 + 0.5*16 = 9
+    w13_s = np.array([[1.0, 1.0], [0.5, 0.5]], np.float32)
+    # W2 [d, W]: one block per 128 output rows; block 0 scale 1, block 1 scale 2
+    w2 = np.zeros((d, W), np.uint8)
+    w2[0, 0], w2[0, 1] = E4[1.0], E4[2.0]                         # y0 = h0 + 2 h1
+    w2[1, 1] = E4[-3.0]                                           # y1 = -3 h1
+    w2[128, 0] = E4[32.0]                                         # y128 = 2 * 32 h0
+    w2[127, 127] = w2[255, 127] = E4[448.0]
+    w2_s = np.array([[1.0], [2.0]], np.float32)
+    r = ffn.expert_forward(a_q, a_s, QuantExpert(w13, w13_s, w2, w2_s))
+
+    g0, g1, u0, u1 = 11.0, -3.0, 2.0, 9.0                          # g2 = 448 has u2 = 0
+    h0 = f32(g0 / (1.0 + math.exp(-g0)) * u0)
+    h1 = f32(g1 / (1.0 + math.exp(-g1)) * u1)
+    assert r["h"][0, 0] == h0 and r["h"][0, 1] == h1 and not r["h"][0, 2:].any()
+    s = f32(h0 / f32(448.0))                                      # amax is h0
+    assert r["h_s"][0, 0] == s
+    # h0 / s lands on 448 (code 0x7E); h1 / s = -1.2805 / 0.049106 = -26.076, whose nearest e4m3
+    # values are -26 (1.625 x 2^4, code 0xDD) and -28: -26
+    q1 = f32(h1 / s)
+    assert -26.25 < q1 < -25.9 and r["h_q"][0, 0] == 0x7E and r["h_q"][0, 1] == 0xDD and not r["h_q"][0, 2:].any()
+    v0, v1 = 448.0 * float(s), -26.0 * float(s)                    # dequantised h
+    want = np.zeros(d)
+    want[0], want[1], want[128] = v0 + 2.0 * v1, -3.0 * v1, 2.0 * 32.0 * v0
+    assert np.array_equal(r["y"][0], want)

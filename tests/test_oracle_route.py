@@ -153,3 +153,36 @@ def test_weights_scale():
     _, w1 = route.select(sc, None, 4, 2, 4)
     _, w2 = route.select(sc, None, 4, 2, 4, routed_scale=2.5)
     assert np.array_equal(w2, (w1 * np.float32(2.5)).astype(np.float32))
+
+
+@pytest.mark.parametrize("case", [(256, 8, 8, 4, 0.0), (256, 8, 8, 4, 0.05), (64, 6, 8, 3, 0.1), (16, 2, 4, 2, 0.2)])
+def test_group_rule_matches_transformers_deepseek_v3_router(case):
+    """The top-2-sum group score, the kept-group mask and the normalised weights against an
+    independent implementation of the same gating: transformers' DeepSeek-V3 router module
+    (library code, not part of the oracle).  Its router is a linear layer followed by the sigmoid;
+    with the hidden size equal to E and an identity weight the linear layer returns its input, so
+    both sides route the same fp32 scores.  Random continuous scores have no ties, so the
+    chosen sets are unique; the weights agree to fp32 rounding of the sum's order."""
+    import torch
+    from transformers.models.deepseek_v3.configuration_deepseek_v3 import DeepseekV3Config
+    from transformers.models.deepseek_v3.modeling_deepseek_v3 import DeepseekV3TopkRouter
+    E, k, G, gk, bscale = case
+    cfg = DeepseekV3Config(hidden_size=E, n_routed_experts=E, num_experts_per_tok=k, n_group=G, topk_group=gk,
+                           norm_topk_prob=True, routed_scaling_factor=1.0)
+    router = DeepseekV3TopkRouter(cfg)
+    logits = (np.random.default_rng(E + k + G).standard_normal((500, E)) * 1.7).astype(np.float32)
+    bias = synth.gen_bias(E, cfg_id=E + k, scale=bscale) if bscale else np.zeros(E, np.float32)
+    with torch.no_grad():
+        router.weight.copy_(torch.eye(E))
+        router.e_score_correction_bias.copy_(torch.from_numpy(bias))
+        lg, w_lib, idx_lib = router(torch.from_numpy(logits))
+        assert torch.equal(lg, torch.from_numpy(logits))
+        scores = torch.sigmoid(torch.from_numpy(logits)).numpy()
+    idx, w = route.select(scores, bias if bscale else None, G, gk, k)
+    idx_lib = idx_lib.numpy()
+    assert np.array_equal(np.sort(idx, 1), np.sort(idx_lib, 1))
+    # weights per expert id: the library returns its slots in its own order
+    order, order_lib = np.argsort(idx, 1), np.argsort(idx_lib, 1)
+    w_by_id = np.take_along_axis(w, order, 1)
+    w_lib_by_id = np.take_along_axis(w_lib.numpy(), order_lib, 1)
+    assert np.allclose(w_by_id, w_lib_by_id, rtol=4 * k * 2.0 ** -24, atol=0)
