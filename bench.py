@@ -374,14 +374,28 @@ def algorithmic_bytes(shape, touched: int) -> dict:
     return {"layer": routed + shared + router + io, "gate_up": gate_up}
 
 
-def cpu_baseline(shape, x_bits, n_tokens: int) -> dict:
-    """The CPU oracle, as it stands, on the first n_tokens of the same workload."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, x_bits, n_tokens: int, repeats: int = 3) -> dict:
+    """The CPU oracle, as it stands, on the first n_tokens of the same workload: the tokens (independent
+    given their routing) are split into one group per host core, each group a plain oracle call in its
+    own thread with BLAS held to one thread, so the run uses exactly the cores the process may run on.
+    Median wall time of `repeats` runs."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     import synth
     from oracle import ffn, route
+    cores = len(os.sched_getaffinity(0))
     x = synth.bf16_bits_to_f32(x_bits[:n_tokens])
     wr = synth.bf16_bits_to_f32(synth.gen_router_w(shape)) if shape.n_experts else None
     bias = synth.skew_bias() if shape.skewed else None
@@ -393,20 +407,154 @@ def cpu_baseline(shape, x_bits, n_tokens: int) -> dict:
     dev = torch.device("cuda:0")
     experts = {}
     from concurrent.futures import ThreadPoolExecutor
-    host = {e: (synth.torch_expert_weight(shape, e, "w13", dev).cpu().numpy(),
-                synth.torch_expert_weight(shape, e, "w2", dev).cpu().numpy()) for e in need}
-    with ThreadPoolExecutor(16) as ex:          # oracle-side weight quantisation: preparation, not timed
-        for e, q in ex.map(lambda e: (e, ffn.quantize_expert(*host[e])), need):
-            experts[e] = q
-    del host
-    t0 = time.perf_counter()
-    ffn.moe_ffn(x, shape.n_experts, shape.top_k, shape.n_group, shape.topk_group, experts.__getitem__, w_router=wr,
-                bias=bias, n_shared=shape.n_shared)
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of {shape.name} (T={shape.tokens}), {len(need)} experts; "
-                      f"{dt:.1f} s of numpy fp64 on the host"}
+    with ThreadPoolExecutor(cores) as ex:       # oracle-side weight quantisation: preparation, not timed
+        for i in range(0, len(need), 32):
+            host = {e: (synth.torch_expert_weight(shape, e, "w13", dev).cpu().numpy(),
+                        synth.torch_expert_weight(shape, e, "w2", dev).cpu().numpy()) for e in need[i:i + 32]}
+            for e, q in ex.map(lambda e: (e, ffn.quantize_expert(*host[e])), list(host)):
+                experts[e] = q
+            del host
+    groups = [g for g in np.array_split(np.arange(n_tokens), cores) if g.size]
+
+    def run(rows):
+        return ffn.moe_ffn(x[rows], shape.n_experts, shape.top_k, shape.n_group, shape.topk_group,
+                           experts.__getitem__, w_router=wr, bias=bias, n_shared=shape.n_shared)
+    times = []
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(len(groups)) as ex:
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            list(ex.map(run, groups))
+            times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"all {n_tokens} tokens of {shape.name} (T={shape.tokens}), {len(need)} experts quantised by "
+                      f"the oracle beforehand (not timed); {len(groups)} token groups in parallel threads, BLAS at "
+                      f"one thread each; median of {repeats} runs: {dt:.1f} s of numpy fp64 on the host "
+                      f"(runs {', '.join(f'{t:.1f}' for t in times)} s)"}
+
+
+def time_workload(shape, steps: int, warmup: int, ue8m0: bool = False, rmsnorm: bool = False,
+                  deterministic: bool = False, with_next_rows: bool = True):
+    """Builds the layer and times `steps` calls of moe_ffn_forward after `warmup` untimed ones.
+    Returns (record, x_bits): the record holds the whole-step timing and rates, the per-stage times
+    and the gate/up GEMM's roofline (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import sparse_moe_ffn_sigmoid_amd as moe
+    import synth
+    from sparse_moe_ffn_sigmoid_amd import _lib
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] {shape.name}: building weights on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    t_build = time.perf_counter()
+    weights = build_layer(shape, dev, ue8m0=ue8m0, rmsnorm=rmsnorm)
+    cfg = moe.MoeConfig.of(shape, ue8m0=ue8m0)
+    x_bits = synth.gen_x(shape)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    T = shape.tokens
+    ws = moe.alloc_workspace(T, cfg, dev)
+    out = torch.empty_like(x)
+    idx = torch.empty((T, max(shape.top_k, 1)), dtype=torch.int32, device=dev)
+    print(f"[bench] weights ready in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
+
+    lib = _lib.load()
+    hip = HipEvents()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    c, wc = cfg.c(), weights.c()
+    flags = moe.MOE_FWD_DETERMINISTIC if deterministic else 0
+    NEV = _lib.MOE_FWD_STAGE_EVENTS
+    evs = [[hip.create() for _ in range(NEV)] for _ in range(steps)]
+    ev_arrays = [(ctypes.c_void_p * NEV)(*[e.value for e in row]) for row in evs]
+    # the timed steps record only the two events around the gate/up GEMM (the roofline kernel):
+    # each event record costs the stream a few microseconds; the other stages are timed after
+    GU0, GU1 = 2, 3
+    ev_gu = [(ctypes.c_void_p * NEV)(*[e.value if j in (GU0, GU1) else None for j, e in enumerate(row)])
+             for row in evs]
+
+    def step(ev_arr):
+        st = lib.moe_ffn_forward_stages(
+            ctypes.c_void_p(x.data_ptr()), T, ctypes.byref(c), ctypes.byref(wc), ctypes.c_void_p(ws.data_ptr()),
+            ws.numel(), ctypes.c_void_p(out.data_ptr()), None,
+            ctypes.c_void_p(idx.data_ptr()) if shape.n_experts else None, None, flags, ev_arr,
+            NEV if ev_arr is not None else 0, stream)
+        if st != 0:
+            raise RuntimeError(f"moe_ffn_forward_stages: {lib.moe_last_error().decode()}")
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t_a, t_b = hip.create(), hip.create()
+    wall0 = time.perf_counter()
+    hip.record(t_a, stream)
+    for i in range(steps):
+        step(ev_gu[i])
+    hip.record(t_b, stream)
+    hip.sync(t_b)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = hip.ms(t_a, t_b) / steps
+    gu_timed = float(np.mean([hip.ms(evs[i][GU0], evs[i][GU1]) for i in range(steps)]))
+    # per-stage breakdown: the same steps again, untimed, with every stage event recorded
+    for i in range(steps):
+        step(ev_arrays[i])
+    torch.cuda.synchronize()
+    names = ["quant_x", "route_permute", "gate_up_gemm", "down_gemm", "combine"]
+    stage = {n: float(np.mean([hip.ms(evs[i][j], evs[i][j + 1]) for i in range(steps)]))
+             for j, n in enumerate(names)}
+    stage["gate_up_gemm"] = gu_timed             # the roofline kernel: from the timed steps
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+
+    if shape.n_experts:
+        loads = np.bincount(idx.cpu().numpy().reshape(-1), minlength=shape.n_experts)
+        touched = int((loads > 0).sum())
+    else:
+        loads = np.zeros(0)
+        touched = 0
+    nbytes = algorithmic_bytes(shape, touched)
+    flops = shape.fp8_flops()
+    t_s = ms_step / 1e3
+    tflops = flops / t_s / 1e12
+    hbm_gbs = nbytes["layer"] / t_s / 1e9
+    gate_up_flops = 2.0 * shape.tokens * (shape.top_k + shape.n_shared) * shape.hidden * 2 * (
+        shape.inter if shape.n_experts else shape.inter_shared)
+    t_gu = stage["gate_up_gemm"] / 1e3
+    ai = gate_up_flops / nbytes["gate_up"]
+    if ai < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": nbytes["gate_up"] / t_gu / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gate_up_flops / t_gu / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(shape) if not (ue8m0 or rmsnorm) else None   # counted on the default
+    roof["kernel"] = gate_up_kernel(shape) + " (gate/up GEMM, SwiGLU + requantisation epilogue)"
+    roof["avg_ms"] = stage["gate_up_gemm"]
+    # the other bound, for the record: the gate/up GEMM's FLOP rate or its algorithmic byte rate
+    roof["hbm_gbs_algorithmic"] = nbytes["gate_up"] / t_gu / 1e9
+    roof["tflops"] = gate_up_flops / t_gu / 1e12
+    attainable = max(flops / (FP8_PEAK_TFLOPS * 1e12), nbytes["layer"] / (HBM_PEAK_GBS * 1e9))
+    rec = {
+        "value": T / t_s, "unit": "tokens/s", "steps": steps, "warmup": warmup, "ms_per_step": ms_step,
+        "config": {"workload": shape.name, "tokens": T, "hidden": shape.hidden, "inter": shape.inter,
+                   "n_experts": shape.n_experts, "top_k": shape.top_k, "n_shared": shape.n_shared,
+                   "inter_shared": shape.inter_shared, "n_group": shape.n_group, "topk_group": shape.topk_group,
+                   "scales": "ue8m0" if ue8m0 else "fp32", "rmsnorm": bool(rmsnorm),
+                   "parallelism": "single GPU"},
+        "fp8_tflops": tflops, "pct_fp8_mfma_peak": 100 * tflops / FP8_PEAK_TFLOPS,
+        "hbm_gbs_algorithmic": hbm_gbs, "pct_hbm_peak": 100 * hbm_gbs / HBM_PEAK_GBS,
+        "frac_attainable_roofline": attainable / t_s, "stages_ms": stage, "wall_s_timed": wall,
+        "experts_touched": touched,
+        "load_max_over_mean": float(loads.max() / loads.mean()) if loads.size else None,
+        "roofline": roof,
+    }
+    if with_next_rows:
+        rec["next_rows"] = next_rows(shape, x, idx, hip, stream, dev)
+    del weights, ws, out, x, idx
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, x_bits
 
 
 def main():
@@ -415,8 +563,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_decode")
-    ap.add_argument("--cpu-tokens", type=int, default=14)   # ~10 s of oracle work at decode shapes
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the workload the CPU oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the V3 prefill sub-record that the default (decode) line carries")
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--ue8m0", action="store_true", help="power-of-two (UE8M0) scales for weights and activations")
     ap.add_argument("--rmsnorm", action="store_true", help="the RMSNorm in front, fused with x's quantisation")
@@ -440,118 +590,22 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    import sparse_moe_ffn_sigmoid_amd as moe
     import synth
-    from sparse_moe_ffn_sigmoid_amd import _lib
-
     shape = synth.SHAPES[args.workload]
-    dev = torch.device("cuda:0")
-    print(f"[bench] {shape.name}: building weights on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
-    t_build = time.perf_counter()
-    weights = build_layer(shape, dev, ue8m0=args.ue8m0, rmsnorm=args.rmsnorm)
-    cfg = moe.MoeConfig.of(shape, ue8m0=args.ue8m0)
-    x_bits = synth.gen_x(shape)
-    x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    T = shape.tokens
-    ws = moe.alloc_workspace(T, cfg, dev)
-    out = torch.empty_like(x)
-    idx = torch.empty((T, max(shape.top_k, 1)), dtype=torch.int32, device=dev)
-    print(f"[bench] weights ready in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
-
-    lib = _lib.load()
-    hip = HipEvents()
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    c, wc = cfg.c(), weights.c()
-    flags = moe.MOE_FWD_DETERMINISTIC if args.deterministic else 0
-    NEV = _lib.MOE_FWD_STAGE_EVENTS
-    evs = [[hip.create() for _ in range(NEV)] for _ in range(args.steps)]
-    ev_arrays = [(ctypes.c_void_p * NEV)(*[e.value for e in row]) for row in evs]
-    # the timed steps record only the two events around the gate/up GEMM (the roofline kernel):
-    # each event record costs the stream a few microseconds; the other stages are timed after
-    GU0, GU1 = 2, 3
-    ev_gu = [(ctypes.c_void_p * NEV)(*[e.value if j in (GU0, GU1) else None for j, e in enumerate(row)])
-             for row in evs]
-
-    def step(ev_arr):
-        st = lib.moe_ffn_forward_stages(
-            ctypes.c_void_p(x.data_ptr()), T, ctypes.byref(c), ctypes.byref(wc), ctypes.c_void_p(ws.data_ptr()),
-            ws.numel(), ctypes.c_void_p(out.data_ptr()), None,
-            ctypes.c_void_p(idx.data_ptr()) if shape.n_experts else None, None, flags, ev_arr,
-            NEV if ev_arr is not None else 0, stream)
-        if st != 0:
-            raise RuntimeError(f"moe_ffn_forward_stages: {lib.moe_last_error().decode()}")
-
-    for _ in range(args.warmup):
-        step(None)
-    torch.cuda.synchronize()
-    t_a, t_b = hip.create(), hip.create()
-    wall0 = time.perf_counter()
-    hip.record(t_a, stream)
-    for i in range(args.steps):
-        step(ev_gu[i])
-    hip.record(t_b, stream)
-    hip.sync(t_b)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = hip.ms(t_a, t_b) / args.steps
-    gu_timed = float(np.mean([hip.ms(evs[i][GU0], evs[i][GU1]) for i in range(args.steps)]))
-    # per-stage breakdown: the same steps again, untimed, with every stage event recorded
-    for i in range(args.steps):
-        step(ev_arrays[i])
-    torch.cuda.synchronize()
-    names = ["quant_x", "route_permute", "gate_up_gemm", "down_gemm", "combine"]
-    stage = {n: float(np.mean([hip.ms(evs[i][j], evs[i][j + 1]) for i in range(args.steps)]))
-             for j, n in enumerate(names)}
-    stage["gate_up_gemm"] = gu_timed             # the roofline kernel: from the timed steps
-
-    if shape.n_experts:
-        loads = np.bincount(idx.cpu().numpy().reshape(-1), minlength=shape.n_experts)
-        touched = int((loads > 0).sum())
-    else:
-        loads = np.zeros(0)
-        touched = 0
-    nbytes = algorithmic_bytes(shape, touched)
-    flops = shape.fp8_flops()
-    t_s = ms_step / 1e3
-    tflops = flops / t_s / 1e12
-    hbm_gbs = nbytes["layer"] / t_s / 1e9
-    gate_up_flops = 2.0 * shape.tokens * (shape.top_k + shape.n_shared) * shape.hidden * 2 * (
-        shape.inter if shape.n_experts else shape.inter_shared)
-    t_gu = stage["gate_up_gemm"] / 1e3
-    ai = gate_up_flops / nbytes["gate_up"]
-    if ai < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "hbm", "achieved": nbytes["gate_up"] / t_gu / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": gate_up_flops / t_gu / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(shape) if not (args.ue8m0 or args.rmsnorm) else None   # counted on the default
-    roof["kernel"] = gate_up_kernel(shape) + " (gate/up GEMM, SwiGLU + requantisation epilogue)"
-    roof["avg_ms"] = stage["gate_up_gemm"]
-    attainable = max(flops / (FP8_PEAK_TFLOPS * 1e12), nbytes["layer"] / (HBM_PEAK_GBS * 1e9))
-
-    res = {
-        "metric": METRIC, "value": T / t_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": shape.name, "tokens": T, "hidden": shape.hidden, "inter": shape.inter,
-                   "n_experts": shape.n_experts, "top_k": shape.top_k, "n_shared": shape.n_shared,
-                   "inter_shared": shape.inter_shared, "n_group": shape.n_group, "topk_group": shape.topk_group,
-                   "scales": "ue8m0" if args.ue8m0 else "fp32", "rmsnorm": bool(args.rmsnorm),
-                   "parallelism": "single GPU"},
-        "fp8_tflops": tflops, "pct_fp8_mfma_peak": 100 * tflops / FP8_PEAK_TFLOPS,
-        "hbm_gbs_algorithmic": hbm_gbs, "pct_hbm_peak": 100 * hbm_gbs / HBM_PEAK_GBS,
-        "frac_attainable_roofline": attainable / t_s, "stages_ms": stage, "wall_s_timed": wall,
-        "experts_touched": touched,
-        "load_max_over_mean": float(loads.max() / loads.mean()) if loads.size else None,
-        "roofline": roof,
-        "next_rows": next_rows(shape, x, idx, hip, stream, dev),
-    }
+    rec, x_bits = time_workload(shape, args.steps, args.warmup, ue8m0=args.ue8m0, rmsnorm=args.rmsnorm,
+                                deterministic=args.deterministic)
+    res = {"metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic"}
+    res.update({k: v for k, v in rec.items() if k not in res and k not in ("steps", "warmup")})
+    if shape.name == "v3_decode" and not args.no_prefill:
+        # the MFMA half of the metric: the V3 prefill step (T = 4096) timed the same way
+        sub, _ = time_workload(synth.V3_PREFILL, max(5, args.steps // 2), max(2, args.warmup), ue8m0=args.ue8m0,
+                               rmsnorm=args.rmsnorm, deterministic=args.deterministic, with_next_rows=False)
+        res["v3_prefill"] = sub
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(shape, x_bits, min(args.cpu_tokens, T))
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(shape, x_bits, min(args.cpu_tokens, shape.tokens))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res))

@@ -75,7 +75,7 @@ def encode(v: np.ndarray) -> np.ndarray:
     out = np.empty(v.shape, dtype=np.uint8)
     fv = v.reshape(-1)
     fo = out.reshape(-1)
-    step = 1 << 16
+    step = 1 << 20
     for i in range(0, fv.size, step):
         fo[i:i + step] = _encode_chunk(fv[i:i + step])
     return out

@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 import synth
-from oracle import ffn, norm, route
+from oracle import e4m3, ffn, norm, permute, quant, route
 
 DEV = torch.device("cuda:0")
 
@@ -61,15 +61,177 @@ def output_bar(got: np.ndarray, ref_bf16: np.ndarray, ref_f64: np.ndarray) -> tu
     return rel, mx, mx_rounded
 
 
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """The bf16 spacing at |v| (normal range): 2^(floor(log2|v|) - 7)."""
+    return 2.0 * bf16_half_ulp(v)
+
+
+def ulp_stats(got: np.ndarray, ref_bf16: np.ndarray) -> tuple[float, float]:
+    """(fraction of elements more than 1 bf16 ulp from the rounded oracle, largest distance in ulps)."""
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref_bf16, np.float64)) / bf16_ulp(ref_bf16)
+    if d.size == 0:
+        return 0.0, 0.0
+    return float((d > 1.0).mean()), float(d.max())
+
+
 def assert_output(got, ref: dict, what="", rows=None):
     rb, rf = ref["out"], ref["out_f64"]
     if rows is not None:
         rb, rf = rb[rows], rf[rows]
     rel, mx, mxr = output_bar(got, rb, rf)
+    frac1, mxu = ulp_stats(got, rb)
     say(f"  {what}: rel L2 {rel:.3e} (vs bf16 oracle), per-element {mx:.3e} x RMS beyond bf16 rounding "
-        f"({mxr:.3e} vs the rounded oracle)")
+        f"({mxr:.3e} vs the rounded oracle); {frac1 * 100:.4f}% of elements > 1 bf16 ulp, max {mxu:.1f} ulp")
     assert rel <= 1e-3, f"{what}: relative L2 {rel:.3e} > 1e-3"
     assert mx <= 2e-2, f"{what}: per-element error {mx:.3e} x RMS > 2e-2"
+
+
+def check_requant(got_q: np.ndarray, got_s: np.ndarray, gu: np.ndarray, absdot: np.ndarray, ue8m0: bool = False,
+                  scale_rtol: float = 2e-6, max_flip: float = 2e-4) -> None:
+    """The GPU's requantised h = silu(gate) * up (codes, 1x128 scales) against the oracle's.
+
+    gu: the oracle's exact gate/up GEMM [M, 2W] (fp64); absdot: sum_k |a_k b_k| of each of its
+    elements.  Both sides round h to fp32 and quantise it, but the GPU accumulates the 128-wide K
+    blocks in fp32 (the oracle in fp64), so its gate and up values are off by at most
+    gamma * absdot, gamma = 256 * 2^-24 (a 128-term fp32 sum inside each block, one scale product
+    and one fused multiply-add per block, with room to spare), and silu, the product and the
+    division by the scale add a few fp32 ulps of the quotient h/s.  A code can therefore differ
+    from the oracle's only where the oracle's quotient lies within that error of an e4m3 rounding
+    midpoint.  So: scales within scale_rtol (UE8M0: equal except where amax sits on a power-of-two
+    boundary); codes equal except for at most max_flip of them; every code that differs is either
+    the same value (+0 / -0) or the other neighbour of the oracle's quotient, whose distance to the
+    midpoint between the two is within the error bound."""
+    from oracle.ffn import silu
+    W = gu.shape[1] // 2
+    g, u = gu[:, :W], gu[:, W:]
+    h = (silu(g) * u).astype(np.float32)
+    want_q, want_s = quant.quant_1x128(h, ue8m0)
+    if ue8m0:
+        assert (got_s != want_s).mean() <= 1e-3
+    else:
+        assert np.allclose(got_s, want_s, rtol=scale_rtol, atol=0), \
+            float(np.max(np.abs(got_s / want_s - 1.0)))
+    same_s = np.repeat(got_s == want_s, 128, axis=1) if ue8m0 else np.ones(h.shape, bool)
+    mism = (got_q != want_q) & same_s
+    assert mism.mean() <= max_flip, mism.mean()
+    if not mism.any():
+        say(f"    requantised h: {h.size} codes, all equal to the oracle's")
+        return
+    r, c = np.nonzero(mism)
+    s_ref = want_s[r, c // 128].astype(np.float64)
+    quot = h[r, c].astype(np.float64) / s_ref
+    gv, wv = e4m3.decode(got_q[r, c]), e4m3.decode(want_q[r, c])
+    grid, _ = e4m3.finite_positive_grid()
+    gi = np.searchsorted(grid, np.abs(gv))
+    wi = np.searchsorted(grid, np.abs(wv))
+    same_value = gv == wv                                                   # +0 and -0
+    neighbours = (np.sign(gv) * np.sign(wv) >= 0) & (np.abs(gi - wi) == 1)
+    neighbours |= (np.minimum(gi, wi) == 0) & (np.maximum(gi, wi) == 1)     # 0 and the smallest subnormal
+    gamma = 256 * 2.0 ** -24
+    zg = g[r, c]
+    sg = 1.0 / (1.0 + np.exp(-zg))
+    dsilu = sg * (1.0 + zg * (1.0 - sg))                                    # d silu / dz
+    err_h = gamma * (np.abs(dsilu * u[r, c]) * absdot[r, c] + np.abs(silu(zg)) * absdot[r, W + c])
+    bound = err_h / s_ref + 16 * 2.0 ** -24 * np.abs(quot) + 2.0 ** -40
+    dist = np.abs(quot - (gv + wv) / 2.0)
+    ok = same_value | (neighbours & (dist <= bound))
+    say(f"    requantised h: {mism.sum()} of {h.size} codes differ ({mism.mean():.2e}): {same_value.sum()} +-0, "
+        f"{(neighbours & ~same_value).sum()} neighbours; midpoint distance / error bound at most "
+        f"{float(np.max(np.where(same_value, 0, dist / bound))):.3f}")
+    for i in np.flatnonzero(~ok)[:10]:
+        say(f"      row {r[i]} col {c[i]}: gpu {got_q[r[i], c[i]]:#04x} ({gv[i]}), oracle {want_q[r[i], c[i]]:#04x} "
+            f"({wv[i]}), quotient {quot[i]!r}, bound {bound[i]:.3e}, h {h[r[i], c[i]]!r}")
+    assert ok.all()
+
+
+# The FP8 MFMA returns a 128-term block sum within this fraction of the block's sum of |products|
+# (measured on MI355X: up to ~1.4e-5 on Gaussian-quantised tiles; the grouped-GEMM tests hold the
+# FP8 path to it).
+FP8_MFMA_REL = 5e-5
+# The exact (bf16 MFMA) gate/up path: fp32 accumulation of 128-term blocks, one scale product and one
+# fused multiply-add per block (see check_requant).
+GAMMA_EXACT = 256 * 2.0 ** -24
+
+
+def expert_error_bound(x_q, x_s, ex: ffn.QuantExpert, ue8m0: bool = False) -> tuple[np.ndarray, np.ndarray]:
+    """For rows (x_q, x_s) of one expert: (bound on |y_gpu - y_oracle| per output element, |y_oracle|).
+
+    The GPU's h may differ from the oracle's only in codes whose quotient h/s lies within the
+    exact path's error of an e4m3 rounding midpoint (see check_requant); each such code may move
+    by its larger neighbour step.  The down GEMM (FP8 MFMA) adds FP8_MFMA_REL of sum_c |h_c w_c|.
+    Built from the oracle's own steps (dequantisation, quantisation, silu) in fp64."""
+    from oracle.ffn import silu
+    A = quant.dequant_1x128(x_q, x_s)
+    W13 = quant.dequant_128x128(ex.w13_q, ex.w13_s)
+    gu = A @ W13.T
+    ad = np.abs(A) @ np.abs(W13).T
+    W = W13.shape[0] // 2
+    del W13
+    g, u = gu[:, :W], gu[:, W:]
+    h = (silu(g) * u).astype(np.float32)
+    h_q, h_s = quant.quant_1x128(h, ue8m0)
+    srep = np.repeat(h_s.astype(np.float64), 128, axis=1)
+    mag = np.abs(h.astype(np.float64)) / srep
+    sg = 1.0 / (1.0 + np.exp(-g))
+    err = GAMMA_EXACT * (np.abs(sg * (1.0 + g * (1.0 - sg)) * u) * ad[:, :W] + np.abs(silu(g)) * ad[:, W:]) / srep
+    # a tile scale off by the amax element's relative error moves every quotient of the tile by as much
+    amax_rel = np.repeat((err * (mag >= 447.0)).reshape(h.shape[0], -1, 128).max(-1) / 448.0, 128, axis=1)
+    err = err + (16 * 2.0 ** -24 + amax_rel) * mag + 2.0 ** -40
+    grid, _ = e4m3.finite_positive_grid()
+    i = np.searchsorted(grid, np.abs(e4m3.decode(h_q)))
+    up = np.where(i + 1 < grid.size, grid[np.minimum(i + 1, grid.size - 1)], np.inf)
+    dn = np.where(i > 0, grid[np.maximum(i - 1, 0)], -np.inf)
+    v = grid[i]
+    near = (np.abs(mag - (v + up) / 2.0) <= err) | (np.abs(mag - (v + dn) / 2.0) <= err)
+    step = np.maximum(np.where(np.isfinite(up), up - v, 0.0), np.where(np.isfinite(dn), v - dn, 0.0))
+    flip = np.where(near, step, 0.0) * srep
+    W2 = np.abs(quant.dequant_128x128(ex.w2_q, ex.w2_s))
+    H = quant.dequant_1x128(h_q, h_s)
+    y_abs = np.abs(H) @ W2.T
+    return FP8_MFMA_REL * y_abs + flip @ W2.T, y_abs
+
+
+def assert_within_error_bound(layer, x_vals, got, ref, rows=None, chunks=8) -> None:
+    """Every output element against a per-element bound on the GPU's deviation from the oracle's fp64
+    output: half a bf16 ulp of the result (output rounding), the fp32 combine's rounding
+    ((k + 2) 2^-24 sum |terms|), |w_gpu - w_oracle| |y| for each routed term, and each expert's
+    expert_error_bound weighted by its routing weight (the shared expert by 1)."""
+    s = layer.s
+    rows = np.arange(x_vals.shape[0]) if rows is None else np.flatnonzero(rows)
+    xr = x_vals[rows] if layer.norm is None else norm.rmsnorm(x_vals[rows], *layer.norm)
+    x_q, x_s = quant.quant_1x128(xr, layer.ue8m0)
+    T = rows.size
+    if s.n_experts:
+        idx, w = ref["topk_idx"][rows], ref["topk_w"][rows].astype(np.float64)
+        dw = np.abs(got["topk_w"][rows].astype(np.float64) - w) if "topk_w" in got else np.zeros_like(w)
+        jobs = [(e, np.flatnonzero((idx == e).any(1))) for e in np.unique(idx)]
+    else:
+        jobs = []
+    if s.n_shared:
+        jobs.append((s.n_experts, np.arange(T)))
+
+    def one(job):
+        e, r = job
+        return e, r, expert_error_bound(x_q[r], x_s[r], layer.expert(int(e)), layer.ue8m0)
+    bound = np.zeros((T, s.hidden))
+    terms = np.zeros((T, s.hidden))
+    with ThreadPoolExecutor(chunks) as ex:
+        for e, r, (b, y_abs) in ex.map(one, jobs):
+            if e == s.n_experts and s.n_shared:
+                wt, dwt = np.ones(r.size), np.zeros(r.size)
+            else:
+                j = np.argmax(idx[r] == e, axis=1)
+                wt, dwt = w[r, j], dw[r, j]
+            bound[r] += wt[:, None] * b + dwt[:, None] * y_abs
+            terms[r] += wt[:, None] * y_abs
+    out = np.asarray(got["out"][rows], np.float64)
+    k = s.top_k if s.n_experts else 0
+    bound += bf16_half_ulp(out) + (k + 2) * 2.0 ** -24 * terms
+    dev = np.abs(out - ref["out_f64"][rows])
+    ratio = dev / bound
+    say(f"    per-element bound: deviation / bound at most {ratio.max():.3f} (median {np.median(ratio):.3f}) "
+        f"over {dev.size} elements")
+    assert np.all(dev <= bound), f"{int((dev > bound).sum())} elements outside the bound"
 
 
 class Layer:
@@ -145,7 +307,10 @@ class Layer:
             self.oracle_experts([e])
         return self._oracle[e]
 
-    def oracle_forward(self, x_vals: np.ndarray, scores: np.ndarray | None = None) -> dict:
+    def oracle_forward(self, x_vals: np.ndarray, scores: np.ndarray | None = None, chunks: int = 1) -> dict:
+        """The oracle layer on x_vals (bf16 values).  With chunks > 1 the tokens (independent given
+        their routing) are split into that many groups run in parallel threads, after every expert
+        they need has been quantised; the routing, output and score arrays are joined."""
         s = self.s
         if s.n_experts:
             if scores is None:
@@ -155,9 +320,18 @@ class Layer:
             self.oracle_experts(list(np.unique(idx)) + [s.n_experts] if s.n_shared else list(np.unique(idx)))
         else:
             self.oracle_experts([0])
-        return ffn.moe_ffn(x_vals, s.n_experts, s.top_k, s.n_group, s.topk_group, self.expert, scores=scores,
-                           bias=self.bias, n_shared=s.n_shared, routed_scale=s.routed_scale, ue8m0=self.ue8m0,
-                           norm=self.norm)
+
+        def run(rows):
+            return ffn.moe_ffn(x_vals[rows], s.n_experts, s.top_k, s.n_group, s.topk_group, self.expert,
+                               scores=None if scores is None else scores[rows], bias=self.bias,
+                               n_shared=s.n_shared, routed_scale=s.routed_scale, ue8m0=self.ue8m0, norm=self.norm)
+        if chunks <= 1 or x_vals.shape[0] < 2:
+            return run(np.arange(x_vals.shape[0]))
+        parts = [p for p in np.array_split(np.arange(x_vals.shape[0]), chunks) if p.size]
+        with ThreadPoolExecutor(len(parts)) as ex:
+            res = list(ex.map(run, parts))
+        keys = ("out", "out_f64") + (("scores", "topk_idx", "topk_w") if s.n_experts else ())
+        return {k: np.concatenate([r[k] for r in res]) for k in keys}
 
 
 def run_layer(layer, xb, scores=None, deterministic=False):
@@ -181,14 +355,15 @@ def run_layer(layer, xb, scores=None, deterministic=False):
     return r
 
 
-def compare_router_run(layer, xb, got, tokens=None):
+def compare_router_run(layer, xb, got, tokens=None, chunks=1):
     """Router on the device: compare tokens whose expert sets agree; the rest must be near-ties."""
     s = layer.s
     xv = synth.bf16_bits_to_f32(xb)
     tok = np.arange(xb.shape[0]) if tokens is None else np.asarray(tokens)
-    ref = layer.oracle_forward(xv[tok])
+    ref = layer.oracle_forward(xv[tok], chunks=chunks)
     if not s.n_experts:
         assert_output(got["out"][tok], ref, f"{s.name} dense")
+        assert_within_error_bound(layer, xv[tok], {"out": got["out"][tok]}, ref, chunks=max(chunks, 4))
         return
     gi = np.sort(got["topk_idx"][tok], 1)
     wi = np.sort(ref["topk_idx"], 1)
@@ -199,3 +374,10 @@ def compare_router_run(layer, xb, got, tokens=None):
     for i in np.flatnonzero(~same):
         assert abs(float(b[i, gi[i]].astype(np.float64).sum() - b[i, wi[i]].astype(np.float64).sum())) < 1e-4
     assert_output(got["out"][tok][same], ref, f"{s.name} (router on device)", rows=same)
+    # the GPU's slots in the oracle's slot order (equal sets; the slot order follows the scores)
+    sub = {"out": got["out"][tok]}
+    if s.n_experts:
+        order = np.argsort(got["topk_idx"][tok], 1)
+        back = np.argsort(np.argsort(ref["topk_idx"], 1), 1)
+        sub["topk_w"] = np.take_along_axis(np.take_along_axis(got["topk_w"][tok], order, 1), back, 1)
+    assert_within_error_bound(layer, xv[tok], sub, ref, rows=same, chunks=max(chunks, 4))

@@ -14,13 +14,13 @@ import pytest
 import torch
 
 import synth
-from oracle import route
+from oracle import permute, route
 
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import sparse_moe_ffn_sigmoid_amd as moe
-    from gpu_util import DEV, Layer, assert_output, bf16_np, say, to_dev
+    from gpu_util import DEV, Layer, assert_output, assert_within_error_bound, bf16_np, say, to_dev
     from gpu_util import compare_router_run as _compare_router_run
     from gpu_util import run_layer as _run
 
@@ -53,6 +53,7 @@ def test_tiny_scores_given_bit_exact_routing(tiny):
     assert np.array_equal(got["topk_idx"], ref["topk_idx"])
     assert np.array_equal(got["topk_w"].view(np.uint32), ref["topk_w"].view(np.uint32))
     assert_output(got["out"], ref, "tiny scores given")
+    assert_within_error_bound(tiny, synth.bf16_bits_to_f32(xb), got, ref)
 
 
 def test_tiny_deterministic_repeat(tiny):
@@ -116,6 +117,7 @@ def test_mid_shapes(shape):
         ref = layer.oracle_forward(synth.bf16_bits_to_f32(xb), scores=sc)
         assert np.array_equal(got["topk_idx"], ref["topk_idx"])
         assert_output(got["out"], ref, f"{shape.name} scores given, deterministic")
+        assert_within_error_bound(layer, synth.bf16_bits_to_f32(xb), got, ref)
 
 
 def test_ragged_tails_empty_experts_and_hot_expert():
@@ -148,17 +150,52 @@ def v3():
     return Layer(synth.V3_PREFILL)
 
 
-def _sample(got_idx, n, seed, must=None):
+def _tile_edges(offsets, bm=128):
+    """Sorted positions of the first and the last row of the m tiles of every group (of its first
+    two and last two tiles when it has more): a group of n rows has ceil(n / bm) tiles over which
+    its rows are split evenly in whole 16-row blocks (the tile kernel's split), keyed by the
+    group's tile row counts (its tile shape)."""
+    shapes = {}
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        c = -(-n // bm)
+        rb = ((-(-n // c)) + 15) // 16 * 16 if c > 1 else bm
+        edges, rows = [], []
+        for j in range(c):
+            a, b = lo + j * rb, min(lo + (j + 1) * rb, hi)
+            if j < 2 or j >= c - 2:
+                edges += [a, b - 1]
+            rows.append(b - a)
+        shapes.setdefault(tuple(rows), []).append(edges)
+    return shapes
+
+
+def _pick_tokens(idx, E, n_min, seed, max_shapes=24):
+    """Tokens whose assignments sit at the first and last rows of the m tiles of one group per tile
+    shape (up to max_shapes shapes, spread over the smallest to the largest), topped up with random
+    tokens to at least n_min."""
+    T, k = idx.shape
+    off, sa, _ = permute.permute(idx, E)
+    shapes = _tile_edges(off)
+    keys = sorted(shapes, key=lambda t: (len(t), t))
+    if len(keys) > max_shapes:
+        keys = [keys[i] for i in np.linspace(0, len(keys) - 1, max_shapes).round().astype(int)]
+    toks = set()
+    for key in keys:
+        for p in shapes[key][0]:
+            toks.add(int(sa[p]) // k)
     r = np.random.default_rng(seed)
-    pick = list(r.choice(got_idx.shape[0], size=n, replace=False))
-    if must is not None and must not in pick:
-        pick[0] = must
-    return sorted(int(p) for p in pick)
+    while len(toks) < n_min:
+        toks.add(int(r.integers(T)))
+    say(f"  {len(toks)} tokens: tile edges of {len(keys)} of {len(shapes)} tile shapes "
+        f"(e.g. {keys[0]}, {keys[len(keys) // 2]}, {keys[-1]}) + random")
+    return sorted(toks)
 
 
-@pytest.mark.parametrize("shape", [synth.V3_DECODE, synth.V3_PREFILL, synth.V3_SKEW])
-def test_v3_sampled_tokens(v3, shape):
-    say(f"forward {shape.name} T={shape.tokens} (sampled oracle check)")
+def _v3_run(v3, shape):
     bias = synth.skew_bias() if shape.skewed else None
     v3.bias = bias
     v3.weights.bias = to_dev(bias) if bias is not None else None
@@ -166,21 +203,42 @@ def test_v3_sampled_tokens(v3, shape):
     got = _run(v3, xb)
     counts = np.bincount(got["topk_idx"].reshape(-1), minlength=256)
     say(f"  loads: max/mean {counts.max() / counts.mean():.1f}, empty experts {(counts == 0).sum()}")
-    hot = int(np.flatnonzero((got["topk_idx"] == counts.argmax()).any(1))[0])
-    _compare_router_run(v3, xb, got, tokens=_sample(got["topk_idx"], 3, shape.cfg_id, must=hot))
+    return xb, got
+
+
+@pytest.mark.timeout(400)
+def test_v3_decode_every_token(v3):
+    """The decode step (T = 64): every token against the oracle."""
+    shape = synth.V3_DECODE
+    say(f"forward {shape.name} T={shape.tokens}: all tokens against the oracle")
+    xb, got = _v3_run(v3, shape)
+    _compare_router_run(v3, xb, got, chunks=8)
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("shape", [synth.V3_PREFILL, synth.V3_SKEW])
+def test_v3_prefill_sampled_tokens(v3, shape):
+    say(f"forward {shape.name} T={shape.tokens} (sampled oracle check)")
+    xb, got = _v3_run(v3, shape)
+    toks = _pick_tokens(got["topk_idx"], 256, 32, shape.cfg_id)
+    _compare_router_run(v3, xb, got, tokens=toks, chunks=8)
     v3.bias = None
     v3.weights.bias = None
 
 
+@pytest.mark.timeout(300)
 def test_dense_ffn_sampled_tokens():
     s = synth.DENSE_FFN
     say(f"forward {s.name} T={s.tokens} (sampled oracle check)")
     layer = Layer(s)
     xb = synth.gen_x(s)
     got = _run(layer, xb)
-    _compare_router_run(layer, xb, got, tokens=[0, 1234, 4095])
+    # 128-row tiles: the first and last row of a spread of tiles, the batch's first and last rows
+    toks = sorted(set([0, s.tokens - 1] + [t for m in range(0, s.tokens, 384) for t in (m, m + 127)]))
+    _compare_router_run(layer, xb, got, tokens=toks, chunks=8)
 
 
+@pytest.mark.timeout(300)
 def test_ep_local_sampled_tokens():
     """One GPU's share of an expert-parallel V3 prefill: 32 local experts, ~1024 rows each."""
     s = synth.V3_EP_LOCAL
@@ -190,4 +248,4 @@ def test_ep_local_sampled_tokens():
     got = _run(layer, xb)
     counts = np.bincount(got["topk_idx"].reshape(-1), minlength=s.n_experts)
     say(f"  rows per expert: min {counts.min()}, max {counts.max()}")
-    _compare_router_run(layer, xb, got, tokens=_sample(got["topk_idx"], 4, s.cfg_id))
+    _compare_router_run(layer, xb, got, tokens=_pick_tokens(got["topk_idx"], s.n_experts, 32, s.cfg_id), chunks=8)
