@@ -121,7 +121,13 @@ typedef struct moe_epi {
   float* h_s;                /* SWIGLU_QUANT: f32 [M][W/128] scales of the output codes      */
   const int32_t* dst_row;    /* WEIGHTED_SCATTER_ADD: destination row of each logical row m */
   const float* row_weight;   /* WEIGHTED_SCATTER_ADD: weight per row m, or NULL (= 1)       */
-  int scale_fmt;             /* SWIGLU_QUANT: MOE_SCALE_* of the output codes' scales        */
+  int scale_fmt;             /* MOE_SCALE_* of every scale of the call.  MOE_SCALE_UE8M0: a_s and
+                                b_s hold powers of two (as fp32 values 2^k, k in [-127, 127]), which
+                                the GEMM applies as the FP8 MFMA's E8M0 scale operands (or in the
+                                exact bf16 conversion of the SwiGLU path) instead of promoting each
+                                K block; SWIGLU_QUANT then also writes power-of-two h_s.  Scales
+                                that are not powers of two give undefined results in this mode.
+                                A NULL epi means MOE_SCALE_F32.                               */
 } moe_epi_t;
 
 MOE_API const char* moe_status_string(int status);

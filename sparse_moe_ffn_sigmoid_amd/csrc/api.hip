@@ -321,12 +321,14 @@ int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int
   sg.N = N;
   sg.K = K;
   sg.out = out;
-  if (epilogue == MOE_EPI_SWIGLU_QUANT) {
+  if (epi) {
     REQUIRE(epi->scale_fmt == MOE_SCALE_F32 || epi->scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG,
             "epi->scale_fmt %d unknown", epi->scale_fmt);
+    sg.pow2_scales = epi->scale_fmt == MOE_SCALE_UE8M0;
+  }
+  if (epilogue == MOE_EPI_SWIGLU_QUANT) {
     sg.out_s = epi->h_s;
     sg.ld_out = N / 2;
-    sg.pow2_scales = epi->scale_fmt == MOE_SCALE_UE8M0;
   } else {
     sg.ld_out = N;
   }
@@ -496,6 +498,7 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
     g0.K = Ws;
     g0.out = routed ? (void*)y_shared : (void*)out;
     g0.ld_out = d;
+    g0.pow2_scales = pow2;
   }
   if (routed) {
     GemmSeg& g1 = dn.seg[1];
@@ -512,6 +515,7 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
     g1.K = W;
     g1.out = y_sorted;
     g1.ld_out = d;
+    g1.pow2_scales = pow2;
   }
   HIP_TRY(launch_grouped_gemm(dn, epi, bm, s), "down GEMM");
   HIP_TRY(mark(4), "event");

@@ -77,6 +77,20 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
   return v8bf{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// The same with the values multiplied by a power of two `scale` during the conversion (gfx950
+// v_cvt_scalef32_pk_bf16_fp8): exact while the scaled values stay in bf16's normal range.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16_scaled(uint32_t w0, uint32_t w1, float scale) {
+  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
+  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
+  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
+  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
+  return v8bf{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// E8M0 byte of a power-of-two fp32 scale 2^k, k in [-127, 127]: the biased exponent k + 127
+// (2^-127 is the fp32 subnormal 0x00400000, whose exponent field 0 is that byte too).
+__device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__float_as_uint(pow2) >> 23); }
+
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll

@@ -218,7 +218,7 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& s
 // the same way.  Wave w covers NTW 16-column tiles of each of the NB B blocks;
 // with NB = 2 (gate/up) a workgroup covers 128 h columns, the SwiGLU
 // requantisation tile.
-template <int NB, int NTW, int P, int EPI>
+template <int NB, int NTW, int P, int EPI, bool SCALED>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   constexpr int NF = NB * NTW;                 // B fragments per lane per K block
   constexpr int CW = 16 * NTW;                 // columns per wave in each B block
@@ -291,40 +291,72 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
         if (kb < nkb) {
           const v8i af = v8i{(int)al[p].x, (int)al[p].y, (int)al[p].z, (int)al[p].w,
                              (int)ah[p].x, (int)ah[p].y, (int)ah[p].z, (int)ah[p].w};
-          v4f part[NF];
-          if constexpr (kExact) {
-            v8bf ab[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ab[j] = e4m3x8_to_bf16((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1]);
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-              const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
-                                  (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
-              v4f t = v4f{0.f, 0.f, 0.f, 0.f};
+          if constexpr (SCALED) {
+            // power-of-two scales: applied exactly by the bf16 conversion (exact path) or as the
+            // FP8 MFMA's E8M0 scale operands, so the MFMA accumulates straight into acc (this lane's
+            // A row, r16, has scale sav[p]; its B column, of block f / NTW, sbv[p][f / NTW])
+            if constexpr (kExact) {
+              v8bf ab[4];
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    ab[j], e4m3x8_to_bf16((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1]), t, 0, 0, 0);
-              part[f] = t;
+                ab[j] = e4m3x8_to_bf16_scaled((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1], sav[p]);
+#pragma unroll
+              for (int f = 0; f < NF; ++f) {
+                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                const float sbf = sbv[p][f / NTW];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      ab[j], e4m3x8_to_bf16_scaled((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1], sbf), acc[f], 0, 0,
+                      0);
+              }
+            } else {
+              const int ea = e8m0_of(sav[p]);
+#pragma unroll
+              for (int f = 0; f < NF; ++f) {
+                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, acc[f], 0, 0, 0, ea, 0,
+                                                                          e8m0_of(sbv[p][f / NTW]));
+              }
             }
           } else {
+            v4f part[NF];
+            if constexpr (kExact) {
+              v8bf ab[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ab[j] = e4m3x8_to_bf16((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1]);
+#pragma unroll
+              for (int f = 0; f < NF; ++f) {
+                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                v4f t = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      ab[j], e4m3x8_to_bf16((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1]), t, 0, 0, 0);
+                part[f] = t;
+              }
+            } else {
+#pragma unroll
+              for (int f = 0; f < NF; ++f) {
+                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                           0, 0, 0);
+              }
+            }
+            // row 4q+i's activation scale sits in lane 4q+i
+            float srow[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) srow[i] = __shfl(sav[p], 4 * q + i);
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-              const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
-                                  (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
-              part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                                         0, 0, 0);
+              const float sbf = sbv[p][f / NTW];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[f][i] = fmaf(part[f][i], srow[i] * sbf, acc[f][i]);
             }
-          }
-          // row 4q+i's activation scale sits in lane 4q+i
-          float srow[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) srow[i] = __shfl(sav[p], 4 * q + i);
-#pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            const float sbf = sbv[p][f / NTW];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[f][i] = fmaf(part[f][i], srow[i] * sbf, acc[f][i]);
           }
           if (kb + P < nkb) STREAM_LOAD(p, kb + P);
         }
@@ -399,6 +431,12 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   }
 }
 
+// The launch's scale format: power-of-two scales when its segments say so (the forward sets both
+// segments alike; the C ABI's GEMM call has one segment).
+static bool gemm_pow2(const GemmArgs& args) {
+  return (args.seg[1].m_tiles > 0 ? args.seg[1] : args.seg[0]).pow2_scales != 0;
+}
+
 static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
   const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
   if (mt == 0) return hipSuccess;
@@ -415,11 +453,20 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
   }
   if (ny == 0) return hipSuccess;
   const dim3 grid(mt, ny);
-  switch (epi) {
-    case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu><<<grid, 256, 0, st>>>(args); break;
-    case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32><<<grid, 256, 0, st>>>(args); break;
-    case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16><<<grid, 256, 0, st>>>(args); break;
-    default: stream_gemm_kernel<1, 2, 4, kEpiScatter><<<grid, 256, 0, st>>>(args); break;
+  if (gemm_pow2(args)) {
+    switch (epi) {
+      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, true><<<grid, 256, 0, st>>>(args); break;
+      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, true><<<grid, 256, 0, st>>>(args); break;
+      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, true><<<grid, 256, 0, st>>>(args); break;
+      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, true><<<grid, 256, 0, st>>>(args); break;
+    }
+  } else {
+    switch (epi) {
+      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, false><<<grid, 256, 0, st>>>(args); break;
+      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, false><<<grid, 256, 0, st>>>(args); break;
+      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, false><<<grid, 256, 0, st>>>(args); break;
+      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, false><<<grid, 256, 0, st>>>(args); break;
+    }
   }
   return hipGetLastError();
 }
@@ -474,7 +521,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int WM, int WN, int MT, int EPI>
+template <int WM, int WN, int MT, int EPI, bool SCALED>
 __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs args) {
   constexpr int NW = WM * WN;                   // waves
   constexpr int NTW = 16 / WN;                  // 16-column tiles per wave (the workgroup covers 256 B rows)
@@ -628,6 +675,32 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
       const int r0 = ab * 16;                   // the lane's rows are r0 + 4q .. +3
       const float4 sa4 = *reinterpret_cast<const float4*>(st - lane_off + A_BYTES + B_BYTES + (r0 >> 5) * 256 +
                                                           (r0 & 31) * 4 + q * 16);
+      if constexpr (SCALED) {
+        // power-of-two scales: the lane's A row r0 + r16 has scale sa_in; applied exactly by the bf16
+        // conversion (exact path) or as the FP8 MFMA's E8M0 scale operands, accumulating into acc
+        const float sa_in = *reinterpret_cast<const float*>(st - lane_off + A_BYTES + B_BYTES + (r0 >> 5) * 256 +
+                                                            ((r0 & 31) + r16) * 4);
+        if constexpr (kExact) {
+          v8bf ab8[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ab8[j] = e4m3x8_to_bf16_scaled((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1], sa_in);
+#pragma unroll
+          for (int f = 0; f < NTW; ++f) {
+            const float sbf = f >= NTW / 2 ? sb1 : sb0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  ab8[j], e4m3x8_to_bf16_scaled((uint32_t)bf[f][2 * j], (uint32_t)bf[f][2 * j + 1], sbf), acc[mi][f], 0,
+                  0, 0);
+          }
+        } else {
+          const int ea = e8m0_of(sa_in), eb = e8m0_of(sb0);
+#pragma unroll
+          for (int f = 0; f < NTW; ++f)
+            acc[mi][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[f], acc[mi][f], 0, 0, 0, ea, 0, eb);
+        }
+        continue;
+      }
       const float c0[4] = {sa4.x * sb0, sa4.y * sb0, sa4.z * sb0, sa4.w * sb0};
       const float c1[4] = {sa4.x * sb1, sa4.y * sb1, sa4.z * sb1, sa4.w * sb1};
       v8bf ab8[4];
@@ -924,7 +997,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 
 template <int WM, int WN, int MT, int EPI>
 static void launch_mfma_cfg(const GemmArgs& args, dim3 grid, hipStream_t st) {
-  mfma_gemm_kernel<WM, WN, MT, EPI><<<grid, 64 * WM * WN, 0, st>>>(args);
+  if (gemm_pow2(args)) mfma_gemm_kernel<WM, WN, MT, EPI, true><<<grid, 64 * WM * WN, 0, st>>>(args);
+  else mfma_gemm_kernel<WM, WN, MT, EPI, false><<<grid, 64 * WM * WN, 0, st>>>(args);
 }
 
 // bm = rows per tile: 32, 64 or 128.  Tiles of 64 or more rows run 8 waves with 64-column

@@ -31,7 +31,9 @@ struct GemmSeg {
   int ld_out;                // elements per output row
   const int32_t* dst_row;    // scatter: destination row per logical row (nullptr = identity)
   const float* row_w;        // scatter: weight per logical row (nullptr = 1)
-  int pow2_scales;           // SwiGLU requantisation: power-of-two (UE8M0) scales when nonzero
+  int pow2_scales;           // nonzero: every scale is a power of two (UE8M0): a_s and b_s enter through the
+                             // MFMA's scale operands (FP8) or the bf16 conversion (exact path) instead of
+                             // a per-block promotion, and the SwiGLU requantisation writes power-of-two scales
 };
 
 struct GemmArgs {
