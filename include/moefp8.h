@@ -278,6 +278,22 @@ MOE_API int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cf
                                    size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w,
                                    int flags, void* const* events, int n_events, void* stream);
 
+/* moe_ffn_forward_noalloc - moe_ffn_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launches, with the workspace taken from a static device array
+ * of MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on (from
+ * the load of its code on that GPU until the process ends).  The call allocates
+ * nothing; the caller still passes x, out and the optional routing outputs.
+ *   Returns MOE_ERR_WORKSPACE (enqueuing nothing) when moe_ffn_workspace_size(T, cfg)
+ *   exceeds MOE_NOALLOC_SCRATCH_BYTES (V3 layer shapes: T <= 223 tokens).
+ *   The array is the current device's (the stream must belong to it).  Every call on
+ *   one GPU shares that GPU's array and leaves its contents behind: calls that
+ *   overlap on one GPU (other streams, other threads) race; serialise them.        */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+MOE_API int moe_ffn_forward_noalloc(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w,
+                                    uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w, int flags,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

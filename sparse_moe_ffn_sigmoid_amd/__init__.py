@@ -8,7 +8,7 @@ library's HIP kernels; there is no fallback when the library is missing.
 Calls (same names as the C ABI in include/moefp8.h):
     fp8_quant_1x128, fp8_quant_128x128, fp8_rmsnorm_quant_1x128, moe_pack_weights, moe_route,
     moe_bias_update, moe_permute, moe_unpermute, fp8_grouped_gemm_blockscaled, moe_ffn_workspace_size,
-    moe_ffn_forward
+    moe_ffn_forward, moe_ffn_forward_noalloc
 """
 from __future__ import annotations
 
@@ -291,4 +291,22 @@ def moe_ffn_forward(x: torch.Tensor, cfg: MoeConfig, weights: MoeWeights, worksp
     _check("moe_ffn_forward", _lib.load().moe_ffn_forward(
         _p(x), T, ctypes.byref(c), ctypes.byref(wc), _p(workspace), workspace.numel(), _p(out), _p(scores),
         _p(topk_idx), _p(topk_w), flags, _stream(x)))
+    return out
+
+
+def moe_ffn_forward_noalloc(x: torch.Tensor, cfg: MoeConfig, weights: MoeWeights, out: torch.Tensor | None = None,
+                            scores: torch.Tensor | None = None, scores_given: bool = False,
+                            topk_idx: torch.Tensor | None = None, topk_w: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_ffn_forward with the library's static device workspace (no workspace argument; the
+    library allocates nothing).  Raises MoeError (MOE_ERR_WORKSPACE) when T needs more than
+    MOE_NOALLOC_SCRATCH_BYTES of workspace.  Calls on one GPU share the array: do not overlap them."""
+    _dev(x, "x")
+    T = x.shape[0]
+    out = torch.empty_like(x) if out is None else out
+    c = cfg.c()
+    wc = weights.c()
+    flags = _lib.MOE_ROUTE_SCORES_GIVEN if scores_given else 0
+    _check("moe_ffn_forward_noalloc", _lib.load().moe_ffn_forward_noalloc(
+        _p(x), T, ctypes.byref(c), ctypes.byref(wc), _p(out), _p(scores), _p(topk_idx), _p(topk_w), flags,
+        _stream(x)))
     return out

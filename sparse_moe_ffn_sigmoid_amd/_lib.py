@@ -22,7 +22,8 @@ MOE_EPI_STORE_F32, MOE_EPI_STORE_BF16, MOE_EPI_SWIGLU_QUANT, MOE_EPI_WEIGHTED_SC
 EXPORTED = ("moe_status_string", "moe_last_error", "fp8_quant_1x128", "fp8_quant_128x128", "moe_route",
             "moe_permute_workspace_size", "moe_permute", "moe_unpermute", "fp8_grouped_gemm_blockscaled",
             "moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_stages", "moe_pack_weights",
-            "fp8_rmsnorm_quant_1x128", "moe_bias_update")
+            "fp8_rmsnorm_quant_1x128", "moe_bias_update", "moe_ffn_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_FWD_STAGE_EVENTS = 6
 
 
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
                                 i, vp]),
         "moe_ffn_forward_stages": (i, [vp, i, ctypes.POINTER(MoeCfgC), ctypes.POINTER(MoeWeightsC), vp, sz, vp, vp,
                                        vp, vp, i, ctypes.POINTER(ctypes.c_void_p), i, vp]),
+        "moe_ffn_forward_noalloc": (i, [vp, i, ctypes.POINTER(MoeCfgC), ctypes.POINTER(MoeWeightsC), vp, vp, vp, vp,
+                                        i, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

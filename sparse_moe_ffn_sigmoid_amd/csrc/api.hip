@@ -3,12 +3,19 @@
 // returns a status; launches are asynchronous on the caller's stream.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
 #include "moefp8.h"
 
 using namespace moefp8;
+
+// Workspace of moe_ffn_forward_noalloc: one array per GPU, allocated when the code object is
+// loaded on that GPU and held until the process ends.  In host code the array's name is only a
+// host-side stand-in: its device address comes from hipGetSymbolAddress, once per device, and
+// only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -130,6 +137,26 @@ FwdLayout fwd_layout(int T, const moe_cfg_t* c) {
   L.y_shared = take(t * d * 4);
   L.total = p;
   return L;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_INVALID_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    REQUIRE(p != nullptr, MOE_ERR_HIP, "no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -360,6 +387,22 @@ int moe_ffn_forward(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_we
                     size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w, int flags,
                     void* stream) {
   return moe_ffn_forward_stages(x, T, cfg, w, ws, ws_bytes, out, scores, topk_idx, topk_w, flags, nullptr, 0, stream);
+}
+
+int moe_ffn_forward_noalloc(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, uint16_t* out,
+                            float* scores, int32_t* topk_idx, float* topk_w, int flags, void* stream) {
+  int st = check_layer_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T %d < 0", T);
+  const size_t need = fwd_layout(T, cfg).total;
+  REQUIRE(need <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+          "T = %d needs %zu bytes of workspace; the static scratch holds %zu (use moe_ffn_forward with a "
+          "caller workspace)", T, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  if (T == 0) return moe_ffn_forward(x, T, cfg, w, nullptr, 0, out, scores, topk_idx, topk_w, flags, stream);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  return moe_ffn_forward(x, T, cfg, w, ws, MOE_NOALLOC_SCRATCH_BYTES, out, scores, topk_idx, topk_w, flags, stream);
 }
 
 int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
