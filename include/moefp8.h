@@ -64,7 +64,7 @@ extern "C" {
 #define MOE_GROUP_SCORE_MAX 1          /* largest biased score of the group                 */
 
 /* ---- scale formats of the 1x128 / 128x128 quantisation ---- */
-#define MOE_SCALE_F32 0                /* s = fp32(amax / 448), correctly rounded              */
+#define MOE_SCALE_F32 0                /* s = max(fp32(amax / 448), 2^-126), correctly rounded */
 #define MOE_SCALE_UE8M0 1              /* s = smallest power of two 2^k >= amax / 448, k in
                                           [-127, 127] (an 8-bit exponent); v / s is then exact */
 
@@ -135,8 +135,8 @@ MOE_API const char* moe_last_error(void);
 
 /* fp8_quant_1x128 - online activation quantisation ([arch blog] "Fine granularity
  * quantization", "Online Quantization").  Per row, per 128 consecutive columns:
- * amax = max |v|; s = fp32(amax / 448) (correctly rounded; 1.0 for an all-zero
- * tile), or with MOE_SCALE_UE8M0 the power of two of MOE_SCALE_UE8M0 ([arch
+ * amax = max |v|; s = fp32(amax / 448) (correctly rounded, at least 2^-126;
+ * 1.0 for an all-zero tile), or with MOE_SCALE_UE8M0 the power of two of MOE_SCALE_UE8M0 ([arch
  * blog] "More customized data format and scaling factor");
  * q = e4m3(fp32(v / s)) rounded to nearest even, saturating.
  *   x      [rows][ld_x] of x_dtype (MOE_DTYPE_BF16 or MOE_DTYPE_F32), cols used

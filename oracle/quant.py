@@ -9,7 +9,10 @@ section bodies are missing from the page, so the oracle takes this reading:
 * weights: one scale per 128x128 block;
 * per tile/block: amax = max |v| (exact), s = fp32(amax / 448) with a
   correctly rounded fp32 division, q_i = E4M3(fp32(v_i / s)) with a correctly
-  rounded fp32 division; an all-zero tile gets s = 1 and codes 0x00.
+  rounded fp32 division; an all-zero tile gets s = 1 and codes 0x00;
+* a tile so small that amax / 448 falls below the smallest normal fp32
+  (amax < 448 * 2^-126) takes s = 2^-126 (the quotient then still lies within
+  +-448, and the scale stays a normal number with a finite reciprocal).
 
 Power-of-two ("UE8M0") variant ([arch blog] heading "More customized data
 format and scaling factor"; the section body is missing, so this is a
@@ -44,7 +47,7 @@ def _scales(amax: np.ndarray, ue8m0: bool = False) -> np.ndarray:
     if ue8m0:
         return _pow2_scales(amax)
     with np.errstate(divide="ignore", invalid="ignore"):
-        s = (amax / F448).astype(np.float32)
+        s = np.maximum((amax / F448).astype(np.float32), np.float32(2.0 ** -126))
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 

@@ -38,13 +38,18 @@ __device__ __forceinline__ uint32_t e4m3_encode4(float v0, float v1, float v2, f
   return e4m3_encode2(v0, v1) | (e4m3_encode2(v2, v3) << 16);
 }
 
-// Scale of one quantisation tile (amax >= 0): fp32(amax / 448), correctly rounded; or, with
-// pow2 (power-of-two "UE8M0" scales), the smallest 2^k, k in [-127, 127], with amax <= 448 * 2^k.
-// For amax = m * 2^E (m in [1, 2)), 448 * 2^k = 1.75 * 2^(k + 8) covers amax exactly when
-// k >= E - 8, or k >= E - 7 when m > 1.75; subnormal amax takes the clamp.  1 for amax == 0.
+// Scale of one quantisation tile (amax >= 0): fp32(amax / 448), correctly rounded, and at least
+// the smallest normal fp32 2^-126 (so that v / s stays within +-448 and 1 / s is finite even for
+// tiles of subnormal values); or, with pow2 (power-of-two "UE8M0" scales), the smallest 2^k,
+// k in [-127, 127], with amax <= 448 * 2^k.  For amax = m * 2^E (m in [1, 2)),
+// 448 * 2^k = 1.75 * 2^(k + 8) covers amax exactly when k >= E - 8, or k >= E - 7 when m > 1.75;
+// subnormal amax takes the clamp.  1 for amax == 0.
 __device__ __forceinline__ float tile_scale(float amax, bool pow2) {
   if (amax == 0.0f) return 1.0f;
-  if (!pow2) return amax / 448.0f;
+  if (!pow2) {
+    const float s = amax / 448.0f;
+    return s < 0x1p-126f ? 0x1p-126f : s;       // (a NaN amax stays NaN)
+  }
   const uint32_t b = __float_as_uint(amax);
   const int ef = (int)(b >> 23);
   int k = ef == 0 ? -127 : ef - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);

@@ -132,7 +132,7 @@ def check_requant(got_q: np.ndarray, got_s: np.ndarray, gu: np.ndarray, absdot: 
     sg = 1.0 / (1.0 + np.exp(-zg))
     dsilu = sg * (1.0 + zg * (1.0 - sg))                                    # d silu / dz
     err_h = gamma * (np.abs(dsilu * u[r, c]) * absdot[r, c] + np.abs(silu(zg)) * absdot[r, W + c])
-    bound = err_h / s_ref + 16 * 2.0 ** -24 * np.abs(quot) + 2.0 ** -40
+    bound = err_h / s_ref + 16 * 2.0 ** -24 * np.abs(quot) + 2.0 ** -149 / s_ref   # (subnormal h: one ulp)
     dist = np.abs(quot - (gv + wv) / 2.0)
     ok = same_value | (neighbours & (dist <= bound))
     say(f"    requantised h: {mism.sum()} of {h.size} codes differ ({mism.mean():.2e}): {same_value.sum()} +-0, "
@@ -176,7 +176,7 @@ def expert_error_bound(x_q, x_s, ex: ffn.QuantExpert, ue8m0: bool = False) -> tu
     err = GAMMA_EXACT * (np.abs(sg * (1.0 + g * (1.0 - sg)) * u) * ad[:, :W] + np.abs(silu(g)) * ad[:, W:]) / srep
     # a tile scale off by the amax element's relative error moves every quotient of the tile by as much
     amax_rel = np.repeat((err * (mag >= 447.0)).reshape(h.shape[0], -1, 128).max(-1) / 448.0, 128, axis=1)
-    err = err + (16 * 2.0 ** -24 + amax_rel) * mag + 2.0 ** -40
+    err = err + (16 * 2.0 ** -24 + amax_rel) * mag + 2.0 ** -149 / srep      # (h subnormal: one ulp of it)
     grid, _ = e4m3.finite_positive_grid()
     i = np.searchsorted(grid, np.abs(e4m3.decode(h_q)))
     up = np.where(i + 1 < grid.size, grid[np.minimum(i + 1, grid.size - 1)], np.inf)

@@ -23,6 +23,8 @@ def _adversarial_rows(seed, rows, cols):
     v[2] *= np.float32(1e30)
     v[3] = np.exp2(r.uniform(-40, 40, cols)).astype(np.float32)  # huge dynamic range inside tiles
     v[4, ::2] = np.float32(-0.0)
+    v[5] *= np.float32(1e-44)                                    # subnormal values: scale clamped to 2^-126
+    v[6] *= np.float32(1e-38)                                    # amax / 448 below the normal range
     return v
 
 
@@ -70,6 +72,8 @@ def test_quant_128x128_bit_exact(rows, cols):
     r = np.random.default_rng(rows + cols)
     w = (r.standard_normal((rows, cols)) * np.exp2(r.integers(-10, 10, (rows, 1)))).astype(np.float32)
     w[:128, :128] = 0.0
+    if cols > 128:
+        w[:128, 128:256] *= np.float32(1e-42)                     # a block of subnormal values
     q, s = moe.fp8_quant_128x128(to_dev(w))
     want_q, want_s = quant.quant_128x128(w)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
@@ -296,7 +300,7 @@ def test_grouped_gemm_bf16_and_scatter(mg):
     assert np.all(np.abs(acc.cpu().numpy() - want) <= FP8_MFMA_REL * bound + 1e-6 * np.abs(want).max())
 
 
-@pytest.mark.parametrize("mg,W,K,wide", [([7, 0, 130], 128, 256, False), ([64] * 5, 256, 512, False),
+@pytest.mark.parametrize("mg,W,K,wide", [([7, 0, 130], 128, 256, "tiny"), ([64] * 5, 256, 512, False),
                                          ([1000], 128, 384, False), ([40, 90], 128, 256, True),
                                          ([130, 0, 75, 200], 256, 768, False), ([66, 128], 128, 128, False),
                                          ([140, 0, 200, 161], 256, 768, False), ([120, 130], 128, 128, False),
@@ -306,7 +310,9 @@ def test_grouped_gemm_bf16_and_scatter(mg):
 def test_grouped_gemm_swiglu_quant(mg, W, K, wide):
     say(f"grouped GEMM SwiGLU+quant G={len(mg)} groups={mg[:8]} W={W} K={K} full-range codes={wide}")
     a_q, a_s, b_q, b_s, off, _ = _gemm_case(W + K, mg, 2 * W, K)
-    if wide:                                   # every finite code, subnormals included, in A
+    if wide == "tiny":                         # rows of activations ~1e-20: h ~1e-40 (subnormal fp32 tiles)
+        a_s[::3] *= np.float32(1e-20)
+    elif wide:                                 # every finite code, subnormals included, in A
         r = np.random.default_rng(8)
         a_q = r.integers(0, 256, a_q.shape).astype(np.uint8)
         a_q[(a_q & 0x7F) == 0x7F] = 0x01

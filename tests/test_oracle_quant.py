@@ -164,3 +164,25 @@ def test_ue8m0_weight_blocks():
     blocks = np.abs(w).reshape(2, 128, 3, 128).max(axis=(1, 3)).astype(np.float64)
     assert np.all(np.frexp(s)[0] == 0.5)
     assert np.all(blocks <= 448 * s) and np.all(448 * s < 2 * blocks)
+
+
+def test_tiles_below_the_normal_range_take_the_smallest_normal_scale():
+    """amax / 448 below the smallest normal fp32: s = 2^-126, and every quotient v / 2^-126 is
+    exact (a power-of-two scaling), so the codes are the e4m3 rounding of v * 2^126 exactly;
+    at amax = 448 * 2^-126 both readings meet; just above it the plain rule applies."""
+    tiny = np.float32(2.0 ** -126)
+    r = np.random.default_rng(11)
+    rows = np.zeros((4, 128), np.float32)
+    rows[0] = (r.standard_normal(128) * 1e-44).astype(np.float32)          # subnormal values
+    rows[1] = (r.standard_normal(128) * 1e-38).astype(np.float32)          # amax / 448 subnormal
+    rows[2] = (r.standard_normal(128) * 1e-40).astype(np.float32)
+    rows[2, 7] = np.float32(448.0) * tiny                                   # amax exactly on the boundary
+    rows[3] = rows[2]
+    rows[3, 7] = np.nextafter(np.float32(448.0) * tiny, np.float32(1.0))    # one ulp above
+    q, s = quant.quant_1x128(rows)
+    assert s[0, 0] == tiny and s[1, 0] == tiny and s[2, 0] == tiny
+    assert s[3, 0] == _nearest_f32(Fraction(float(rows[3, 7])) / 448) and s[3, 0] > tiny
+    for i in range(3):
+        exact = rows[i].astype(np.float64) * 2.0 ** 126          # exact in fp64, signed zeros kept
+        assert np.all(np.abs(exact) <= 448.0)
+        assert np.array_equal(q[i], e4m3.encode(exact))
