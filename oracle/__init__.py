@@ -32,4 +32,4 @@ something other than itself (closed forms, brute force, library routines,
 invariants).  One part has no such pin and is marked "parity unpinned": the
 fidelity of the FP8 layer to unquantised math (the pages' claim is cut off).
 """
-from . import e4m3, quant, route, permute, gemm, ffn, calibrate  # noqa: F401
+from . import e4m3, quant, route, permute, gemm, ffn, calibrate, backward  # noqa: F401
