@@ -98,14 +98,12 @@ __device__ void locate_tile(const GemmSeg& sd, int bm, const GroupTiles& s, int 
   count = __builtin_amdgcn_readfirstlane(count);
 }
 
-// Maps blockIdx.x to (segment, group, first row, end row) for tiles of bm
-// rows (one workgroup per m tile; blockIdx.y is the n tile).  Static segment
-// tiles come first.  Returns false (uniformly) for workgroups past the real
+// Maps m tile v to (segment, group, first row, end row) for tiles of bm rows (one
+// workgroup per m tile and n tile).  Static segment tiles come first.  Returns false (uniformly) for workgroups past the real
 // tile count.  The tile coordinates are workgroup-uniform: readfirstlane lets
 // the compiler keep them (and every address derived from them) in scalar
 // registers.
-__device__ bool find_tile(const GemmArgs& args, int bm, int& si, int& g, int& m0, int& m_end) {
-  int v = blockIdx.x;
+__device__ bool find_tile(const GemmArgs& args, int bm, int v, int& si, int& g, int& m0, int& m_end) {
   if (v < args.seg[0].m_tiles) {
     si = 0;
     g = 0;
@@ -218,7 +216,15 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& s
 // the same way.  Wave w covers NTW 16-column tiles of each of the NB B blocks;
 // with NB = 2 (gate/up) a workgroup covers 128 h columns, the SwiGLU
 // requantisation tile.
-template <int NB, int NTW, int P, int EPI, bool SCALED>
+// NFAST: the grid is (n tiles, m tiles) with the n tile fastest-varying, so that a tile's n tiles
+// are dispatched together and the static segment's first.  Workgroups go to the 8 XCDs
+// round-robin by linear id, so with a multiple of 8 n tiles the m tiles of one n tile, which
+// stream the same weights, run on one XCD at about the same time and share its L2: the shared
+// expert's rows (T of them in T / 16 tiles) then read its weights from HBM about once.  Measured
+// for the gate/up GEMM at decode (T = 64): 6.372 GB fetched per launch instead of 6.438 GB for
+// 6.343 GB of algorithmic bytes, 0.924 instead of 0.935 ms.  The down GEMM ran 2.5% slower in
+// that order, and keeps the grid (m tiles, n tiles).
+template <int NB, int NTW, int P, int EPI, bool SCALED, bool NFAST>
 __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   constexpr int NF = NB * NTW;                 // B fragments per lane per K block
   constexpr int CW = 16 * NTW;                 // columns per wave in each B block
@@ -232,12 +238,12 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r16 = lane & 15,
             q = lane >> 4;
   int si, g, m0, m_end;
-  if (!find_tile(args, 16, si, g, m0, m_end)) return;
+  if (!find_tile(args, 16, NFAST ? blockIdx.y : blockIdx.x, si, g, m0, m_end)) return;
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& s1 = args.seg[1];
   const int K = si ? s1.K : s0.K, nkb = K >> 7;
   const int half = (si ? s1.N : s0.N) / NB;
-  const int nbase = blockIdx.y * 4 * CW;        // first column of this workgroup in each block
+  const int nbase = (NFAST ? blockIdx.x : blockIdx.y) * 4 * CW;   // first column of this workgroup in each block
   if (nbase >= half) return;
   const int ncol0 = nbase + wave * CW;         // first column of this wave in each block
   const bool wave_live = ncol0 < half;          // all waves live when half % (4 CW) == 0
@@ -452,20 +458,20 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
     }
   }
   if (ny == 0) return hipSuccess;
-  const dim3 grid(mt, ny);
+  const dim3 grid(ny, mt), grid_m(mt, ny);
   if (gemm_pow2(args)) {
     switch (epi) {
-      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, true><<<grid, 256, 0, st>>>(args); break;
-      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, true><<<grid, 256, 0, st>>>(args); break;
-      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, true><<<grid, 256, 0, st>>>(args); break;
-      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, true><<<grid, 256, 0, st>>>(args); break;
+      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, true, true><<<grid, 256, 0, st>>>(args); break;
+      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, true, false><<<grid_m, 256, 0, st>>>(args); break;
+      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, true, false><<<grid_m, 256, 0, st>>>(args); break;
+      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, true, false><<<grid_m, 256, 0, st>>>(args); break;
     }
   } else {
     switch (epi) {
-      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, false><<<grid, 256, 0, st>>>(args); break;
-      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, false><<<grid, 256, 0, st>>>(args); break;
-      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, false><<<grid, 256, 0, st>>>(args); break;
-      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, false><<<grid, 256, 0, st>>>(args); break;
+      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, false, true><<<grid, 256, 0, st>>>(args); break;
+      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, false, false><<<grid_m, 256, 0, st>>>(args); break;
+      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, false, false><<<grid_m, 256, 0, st>>>(args); break;
+      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, false, false><<<grid_m, 256, 0, st>>>(args); break;
     }
   }
   return hipGetLastError();
