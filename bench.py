@@ -28,6 +28,8 @@ Helpers for the counter runs:
                            profiles/<workload>_gate_up_traffic.md.
   --mfma-summary DIR       turns the MFMA counter run under DIR (mfma/) and a bench line
                            (DIR/bench.json) into profiles/<workload>_mfma_utilization.md.
+  --trace-summary DIR      turns a rocprofv3 --kernel-trace --stats run under DIR (ktrace/) and
+                           its bench line (DIR/bench.json) into profiles/<workload>_kernel_trace.md.
 """
 from __future__ import annotations
 
@@ -133,15 +135,17 @@ def gemm_source_hash() -> str:
     return h.hexdigest()
 
 
-def gate_up_kernel(shape) -> str:
+def gate_up_kernel(shape, ue8m0: bool = False) -> str:
     """Name of the kernel the library runs for the gate/up GEMM of this shape (the library picks
     the weight-streaming kernel when groups average at most 16 rows, else the MFMA tile kernel
-    with 64 rows per wave for groups above 64 rows)."""
+    with 64 rows per wave for groups above 64 rows; the template argument after the epilogue says
+    whether the scales are powers of two)."""
     rows = shape.tokens * shape.top_k / shape.n_experts if shape.n_experts else shape.tokens
+    scaled = "true" if ue8m0 else "false"
     if rows <= 16:
-        return "stream_gemm_kernel<2, 2, 6, 2>"
+        return f"stream_gemm_kernel<2, 2, 6, 2, {scaled}, true>"
     mt = 1 if rows <= 32 else 2 if rows <= 64 else 4
-    return f"mfma_gemm_kernel<2, {4 if mt >= 2 else 2}, {mt}, 2>"
+    return f"mfma_gemm_kernel<2, {4 if mt >= 2 else 2}, {mt}, 2, {scaled}>"
 
 
 def traffic_file(shape) -> str:
@@ -244,7 +248,7 @@ def mfma_summary(d: str, shape) -> None:
         grbm = sum(e["GRBM_GUI_ACTIVE"]) / n
         ns = sum(e["_ns"].values()) / len(e["_ns"])
         frac = busy / (grbm / 8 * 1024)
-        is_gu = name.endswith(", 2>")
+        is_gu = name.split("<")[1].split(",")[-2].strip() == "2"     # the epilogue argument: SwiGLU
         ms = live["stages_ms"]["gate_up_gemm" if is_gu else "down_gemm"]
         fl = gu if is_gu else dn
         tf = fl / (ms * 1e-3) / 1e12
@@ -300,6 +304,47 @@ def traffic_summary(d: str, shape) -> None:
     with open(traffic_file(shape), "w") as fh:
         fh.write("\n".join(lines))
     print(f"wrote {traffic_file(shape)}: {traffic / 1e9:.3f} GB per launch")
+
+
+def trace_summary(d: str, shape) -> None:
+    """Turns a `rocprofv3 --kernel-trace --stats` run of this workload's bench (DIR/ktrace, its bench
+    line in DIR/bench.json) into profiles/<workload>_kernel_trace.md."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "ktrace", "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}/ktrace")
+    rows = list(csv.DictReader(open(files[0])))
+    live = json.loads(open(os.path.join(d, "bench.json")).read().strip().splitlines()[-1])
+    layer, prep = [], []
+    prep_marks = ("at::native", "quant_128x128", "pack_kernel", "copyBuffer", "perm_gather")
+    for r in rows:
+        name = r["Name"].replace("void ", "").replace("moefp8::", "").split("(")[0]
+        short = name if len(name) <= 60 else name[:60] + "\u2026"
+        line = (f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                f"{float(r['MaxNs']) / 1e3:.1f} |")
+        (prep if any(m in r["Name"] for m in prep_marks) else layer).append(line)
+    steps, warm = live["steps"], live["warmup"]
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv -d $OUT/ktrace -o kt -- "
+           f"python3 $R/bench.py --workload {shape.name} --steps {steps} --warmup {warm} --no-cpu-baseline --no-prefill "
+           f"> $OUT/bench.json")
+    st = live["stages_ms"]
+    lines = [
+        f"# Kernel trace, {shape.name} (`moe_ffn_forward`; {warm} warm-up + {steps} timed + {steps} stage-timing calls)",
+        "", "Commands (R = repository root, OUT = the directory the run writes to):", "", "```", cmd,
+        f"python3 $R/bench.py --workload {shape.name} --trace-summary $OUT", "```", "",
+        "Per-launch durations from `kt_kernel_stats.csv` (the layer's kernels; weight preparation before the",
+        "timed region is listed apart).", "",
+        "| kernel | calls | average µs | min µs | max µs |", "|---|---|---|---|---|", *layer, "",
+        "Weight preparation (not timed):", "", "| kernel | calls | average µs | min µs | max µs |", "|---|---|---|---|---|",
+        *prep, "", "The same run's bench line (HIP events on the launch stream):", "", "```",
+        f"ms_per_step: {live['ms_per_step']:.4f}",
+        "stages_ms: " + ", ".join(f"{k} {v:.4f}" for k, v in st.items()),
+        f"roofline kernel: {live['roofline']['kernel']}, avg_ms {live['roofline']['avg_ms']:.4f}", "```", ""]
+    out = os.path.join(ROOT, "profiles", f"{shape.name}_kernel_trace.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {out}")
 
 
 def norm_weight(shape, dev):
@@ -529,7 +574,7 @@ def time_workload(shape, steps: int, warmup: int, ue8m0: bool = False, rmsnorm: 
         roof = {"bound": "mfma", "achieved": gate_up_flops / t_gu / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(shape) if not (ue8m0 or rmsnorm) else None   # counted on the default
-    roof["kernel"] = gate_up_kernel(shape) + " (gate/up GEMM, SwiGLU + requantisation epilogue)"
+    roof["kernel"] = gate_up_kernel(shape, ue8m0) + " (gate/up GEMM, SwiGLU + requantisation epilogue)"
     roof["avg_ms"] = stage["gate_up_gemm"]
     # the other bound, for the record: the gate/up GEMM's FLOP rate or its algorithmic byte rate
     roof["hbm_gbs_algorithmic"] = nbytes["gate_up"] / t_gu / 1e9
@@ -557,6 +602,87 @@ def time_workload(shape, steps: int, warmup: int, ue8m0: bool = False, rmsnorm: 
     return rec, x_bits
 
 
+def time_backward(shape, steps: int, warmup: int) -> dict:
+    """The FP8 backward of the routed experts' two grouped GEMMs at this workload's routing, timed
+    as one pass: dgrad of the down projection (dH = dY . W2: dY 1x128-quantised, W2^T packed),
+    its wgrad (dW2_e = dY_e^T . H_e: both 128x1-quantised per expert), dgrad of gate/up
+    (dX = dGU . W13) and its wgrad (dW13_e = dGU_e^T . X_e), with every quantisation inside the
+    timed region; fp32 weight gradients.  The gradients dY, dGU and the activations H, X are seeded
+    synthetic rows (N(0, 1), bf16) in the routing's sorted order; the SwiGLU, combine and router
+    backward steps are not part of it."""
+    import numpy as np
+    import torch
+
+    import sparse_moe_ffn_sigmoid_amd as moe
+    import synth
+    dev = torch.device("cuda:0")
+    E, d, W, k, T = shape.n_experts, shape.hidden, shape.inter, shape.top_k, shape.tokens
+    cfg = moe.MoeConfig.of(shape)
+    xb = torch.from_numpy(synth.gen_x(shape).view(np.int16)).to(dev).view(torch.bfloat16)
+    wr = torch.from_numpy(synth.gen_router_w(shape).view(np.int16)).to(dev).view(torch.bfloat16)
+    _, idx, _ = moe.moe_route(cfg, T, dev, x=xb, w_router=wr)
+    offsets = moe.moe_permute(idx, E)[0]
+    M = T * k
+    print(f"[bench] backward {shape.name}: transposing the expert weights", file=sys.stderr, flush=True)
+    w2t_q = torch.empty((E, W, d), dtype=torch.uint8, device=dev)
+    w2t_s = torch.empty((E, W // 128, d // 128), dtype=torch.float32, device=dev)
+    w13t_q = torch.empty((E, d, 2 * W), dtype=torch.uint8, device=dev)
+    w13t_s = torch.empty((E, d // 128, 2 * W // 128), dtype=torch.float32, device=dev)
+    for e in range(E):
+        q2, s2 = moe.fp8_quant_128x128(synth.torch_expert_weight(shape, e, "w2", dev))
+        w2t_q[e], w2t_s[e] = moe.moe_pack_weights_transposed(q2, s2)
+        q13, s13 = moe.fp8_quant_128x128(synth.torch_expert_weight(shape, e, "w13", dev))
+        w13t_q[e], w13t_s[e] = moe.moe_pack_weights_transposed(q13, s13)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.stream_seed(shape.cfg_id, 9))
+    dy = torch.randn((M, d), generator=gen, device=dev).to(torch.bfloat16)
+    h = torch.randn((M, W), generator=gen, device=dev).to(torch.bfloat16)
+    dgu = torch.randn((M, 2 * W), generator=gen, device=dev).to(torch.bfloat16)
+    xs = torch.randn((M, d), generator=gen, device=dev).to(torch.bfloat16)
+    dw2 = torch.empty((E, d, W), dtype=torch.float32, device=dev)
+    dw13 = torch.empty((E, 2 * W, d), dtype=torch.float32, device=dev)
+    dh = torch.empty((M, W), dtype=torch.float32, device=dev)
+    dx = torch.empty((M, d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        q, s = moe.fp8_quant_1x128(dy)
+        moe.fp8_grouped_gemm_blockscaled(q, s, w2t_q, w2t_s, offsets, moe.MOE_EPI_STORE_F32, m_max=M, out=dh)
+        a, as_, po = moe.fp8_quant_128x1_grouped(dy, offsets)
+        b, bs, _ = moe.fp8_quant_128x1_grouped(h, offsets)
+        moe.fp8_grouped_gemm_wgrad(a, as_, b, bs, po, M, out=dw2)
+        q, s = moe.fp8_quant_1x128(dgu)
+        moe.fp8_grouped_gemm_blockscaled(q, s, w13t_q, w13t_s, offsets, moe.MOE_EPI_STORE_F32, m_max=M, out=dx)
+        a, as_, po = moe.fp8_quant_128x1_grouped(dgu, offsets)
+        b, bs, _ = moe.fp8_quant_128x1_grouped(xs, offsets)
+        moe.fp8_grouped_gemm_wgrad(a, as_, b, bs, po, M, out=dw13)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record()
+    for _ in range(steps):
+        step()
+    b_ev.record()
+    torch.cuda.synchronize()
+    ms = a_ev.elapsed_time(b_ev) / steps
+    flops = 2.0 * M * d * W * 2 + 2.0 * M * d * 2 * W * 2          # dgrad + wgrad of both GEMMs
+    grad_bytes = 4.0 * E * 3 * d * W                                  # the fp32 weight gradients written
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "fp8_tflops": tf,
+           "pct_fp8_mfma_peak": 100 * tf / FP8_PEAK_TFLOPS,
+           "weight_grad_write_gbs": grad_bytes / (ms * 1e-3) / 1e9,
+           "pct_hbm_peak_weight_grads": 100 * grad_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "steps": steps, "warmup": warmup,
+           "scope": "routed experts' dgrad + wgrad of gate/up and down with their 1x128 / 128x1 quantisations; "
+                    "fp32 weight gradients; synthetic gradients"}
+    del w2t_q, w13t_q, dw2, dw13, dh, dx
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -573,7 +699,13 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB")
     ap.add_argument("--traffic-summary", metavar="DIR")
     ap.add_argument("--mfma-summary", metavar="DIR")
+    ap.add_argument("--trace-summary", metavar="DIR")
+    ap.add_argument("--backward", action="store_true", help="time only the FP8 backward GEMMs of the workload")
     args = ap.parse_args()
+    if args.trace_summary:
+        import synth
+        trace_summary(args.trace_summary, synth.SHAPES[args.workload])
+        return
     if args.mfma_summary:
         import synth
         mfma_summary(args.mfma_summary, synth.SHAPES[args.workload])
@@ -592,6 +724,9 @@ def main():
 
     import synth
     shape = synth.SHAPES[args.workload]
+    if args.backward:
+        print(json.dumps({"workload": shape.name, "backward": time_backward(shape, args.steps, args.warmup)}))
+        return
     rec, x_bits = time_workload(shape, args.steps, args.warmup, ue8m0=args.ue8m0, rmsnorm=args.rmsnorm,
                                 deterministic=args.deterministic)
     res = {"metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -603,6 +738,7 @@ def main():
         sub, _ = time_workload(synth.V3_PREFILL, max(5, args.steps // 2), max(2, args.warmup), ue8m0=args.ue8m0,
                                rmsnorm=args.rmsnorm, deterministic=args.deterministic, with_next_rows=False)
         res["v3_prefill"] = sub
+        res["v3_prefill_backward"] = time_backward(synth.V3_PREFILL, max(3, args.steps // 10), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(shape, x_bits, min(args.cpu_tokens, shape.tokens))

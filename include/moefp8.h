@@ -278,6 +278,52 @@ MOE_API int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cf
                                    size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w,
                                    int flags, void* const* events, int n_events, void* stream);
 
+/* ---- FP8 backward of the grouped GEMMs ([arch blog] "First ever FP8 Precision OSS LLM
+ * pre-training": the model trains with FP8 matrix multiplications; the section stops after its
+ * motivation, so the following is a reading).  For a forward GEMM C_g = A_g . W_g^T over group
+ * g's rows (A 1x128-quantised, W in 128x128 blocks):
+ *   dgrad  dA = dC . W: fp8_quant_1x128 of dC along its contraction dimension, then
+ *          fp8_grouped_gemm_blockscaled with W^T from moe_pack_weights_transposed (W's 128x128
+ *          blocks read transposed, with the same scales);
+ *   wgrad  dW_g = dC_g^T . A_g, a contraction over the group's rows: fp8_quant_128x1_grouped of
+ *          dC and of A (128x1 tiles: per column, per 128 rows of one group), then
+ *          fp8_grouped_gemm_wgrad.  ---- */
+
+/* moe_padded_rows - an upper bound of the padded row count of M rows in G groups, each group
+ * padded to a multiple of 128: (ceil(M / 128) + G) * 128 (0 on invalid arguments). */
+MOE_API size_t moe_padded_rows(int M, int G);
+
+/* fp8_quant_128x1_grouped - transposed ("128x1") tile quantisation for wgrad.  x [M][ld_x]
+ * (x_dtype MOE_DTYPE_BF16 or MOE_DTYPE_F32, N columns used), rows grouped by offsets i32 [G+1]
+ * (device, offsets[G] = M).  Each group is padded to a multiple of 128 rows; padded_offsets
+ * i32 [G+1] (device, written) receives the padded offsets.  Output, transposed: q_t e4m3 [N][ld_q]
+ * with q_t[n][padded[g] + r] the code of x[offsets[g] + r][n] (zeros in a group's padding),
+ * s_t f32 [N][ld_q / 128], one scale per column and 128 padded rows, by the rule of
+ * fp8_quant_1x128.  N % 128 == 0; ld_q % 128 == 0 and ld_q >= moe_padded_rows(M, G) (columns
+ * past padded[G] are not written).  1 <= G <= 1024.                                      */
+MOE_API int fp8_quant_128x1_grouped(const void* x, int x_dtype, int M, int N, int ld_x, const int32_t* offsets,
+                                    int G, int32_t* padded_offsets, uint8_t* q_t, int ld_q, float* s_t,
+                                    int scale_fmt, void* stream);
+
+/* moe_pack_weights_transposed - weight preparation for dgrad: row-major e4m3 W [G][N][K] with
+ * 128x128 block scales w_s f32 [G][N/128][K/128] -> W^T [G][K][N] in the MFMA-fragment order of
+ * moe_pack_weights, and its scales wt_s f32 [G][K/128][N/128] (the same blocks, transposed).
+ * N % 128 == 0, K % 128 == 0; the outputs must not overlap the inputs.                     */
+MOE_API int moe_pack_weights_transposed(const uint8_t* w_q, const float* w_s, int G, int N, int K, uint8_t* wt_q,
+                                        float* wt_s, void* stream);
+
+/* fp8_grouped_gemm_wgrad - per group g:
+ *   out[g][i][j] = sum over kb of a_ts[i][kb] * b_ts[j][kb] * sum_{k in kb} A_t[i][k] * B_t[j][k]
+ * over the 128-wide K blocks kb of the group's padded rows [padded[g], padded[g+1]) (fp32
+ * accumulation, FP8 MFMA; power-of-two scales with MOE_SCALE_UE8M0 go in as the MFMA's E8M0
+ * operands).  a_t e4m3 [Na][ld], a_ts f32 [Na][ld/128], b_t e4m3 [Nb][ld], b_ts f32
+ * [Nb][ld/128] (from fp8_quant_128x1_grouped); padded_offsets i32 [G+1] (device); M the rows
+ * before padding (bounds the padded rows); out f32 [G][Na][Nb] (a group without rows gets
+ * zeros).  Na % 128 == 0, Nb % 128 == 0, ld as for fp8_quant_128x1_grouped.               */
+MOE_API int fp8_grouped_gemm_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_t, const float* b_ts,
+                                   const int32_t* padded_offsets, int G, int M, int Na, int Nb, int ld, float* out,
+                                   int scale_fmt, void* stream);
+
 /* moe_ffn_forward_noalloc - moe_ffn_forward for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same launches, with the workspace taken from a static device array

@@ -8,7 +8,8 @@ library's HIP kernels; there is no fallback when the library is missing.
 Calls (same names as the C ABI in include/moefp8.h):
     fp8_quant_1x128, fp8_quant_128x128, fp8_rmsnorm_quant_1x128, moe_pack_weights, moe_route,
     moe_bias_update, moe_permute, moe_unpermute, fp8_grouped_gemm_blockscaled, moe_ffn_workspace_size,
-    moe_ffn_forward, moe_ffn_forward_noalloc
+    moe_ffn_forward, moe_ffn_forward_noalloc, moe_padded_rows, fp8_quant_128x1_grouped,
+    moe_pack_weights_transposed, fp8_grouped_gemm_wgrad
 """
 from __future__ import annotations
 
@@ -296,7 +297,8 @@ def moe_ffn_forward(x: torch.Tensor, cfg: MoeConfig, weights: MoeWeights, worksp
 
 def moe_ffn_forward_noalloc(x: torch.Tensor, cfg: MoeConfig, weights: MoeWeights, out: torch.Tensor | None = None,
                             scores: torch.Tensor | None = None, scores_given: bool = False,
-                            topk_idx: torch.Tensor | None = None, topk_w: torch.Tensor | None = None) -> torch.Tensor:
+                            topk_idx: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
+                            deterministic: bool = False) -> torch.Tensor:
     """moe_ffn_forward with the library's static device workspace (no workspace argument; the
     library allocates nothing).  Raises MoeError (MOE_ERR_WORKSPACE) when T needs more than
     MOE_NOALLOC_SCRATCH_BYTES of workspace.  Calls on one GPU share the array: do not overlap them."""
@@ -305,8 +307,65 @@ def moe_ffn_forward_noalloc(x: torch.Tensor, cfg: MoeConfig, weights: MoeWeights
     out = torch.empty_like(x) if out is None else out
     c = cfg.c()
     wc = weights.c()
-    flags = _lib.MOE_ROUTE_SCORES_GIVEN if scores_given else 0
+    flags = (_lib.MOE_ROUTE_SCORES_GIVEN if scores_given else 0) | (MOE_FWD_DETERMINISTIC if deterministic else 0)
     _check("moe_ffn_forward_noalloc", _lib.load().moe_ffn_forward_noalloc(
         _p(x), T, ctypes.byref(c), ctypes.byref(wc), _p(out), _p(scores), _p(topk_idx), _p(topk_w), flags,
         _stream(x)))
+    return out
+
+
+# ---- FP8 backward of the grouped GEMMs ----
+
+def moe_padded_rows(M: int, G: int) -> int:
+    """Upper bound of the rows of M rows in G groups once every group is padded to 128 rows."""
+    return int(_lib.load().moe_padded_rows(M, G))
+
+
+def fp8_quant_128x1_grouped(x: torch.Tensor, offsets: torch.Tensor, ue8m0: bool = False):
+    """x [M, N] bf16 or fp32, rows grouped by offsets int32 [G+1] -> (q_t uint8 [N, Mp], s_t fp32
+    [N, Mp/128], padded offsets int32 [G+1]): 128x1 tiles per column and group, stored transposed
+    (Mp = moe_padded_rows(M, G); columns past the padded rows are left unwritten)."""
+    _dev(x, "x")
+    _dev(offsets, "offsets")
+    M, N = x.shape
+    G = offsets.numel() - 1
+    dt = {torch.bfloat16: _lib.MOE_DTYPE_BF16, torch.float32: _lib.MOE_DTYPE_F32}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be bfloat16 or float32")
+    mp = moe_padded_rows(M, G)
+    q = torch.empty((N, mp), dtype=torch.uint8, device=x.device)
+    s = torch.empty((N, mp // 128), dtype=torch.float32, device=x.device)
+    po = torch.empty(G + 1, dtype=torch.int32, device=x.device)
+    _check("fp8_quant_128x1_grouped", _lib.load().fp8_quant_128x1_grouped(
+        _p(x), dt, M, N, N, _p(offsets), G, _p(po), _p(q), mp, _p(s), _fmt(ue8m0), _stream(x)))
+    return q, s, po
+
+
+def moe_pack_weights_transposed(w_q: torch.Tensor, w_s: torch.Tensor):
+    """Row-major e4m3 W [G, N, K] (or [N, K]) with block scales [G, N/128, K/128] -> W^T in the
+    GEMMs' fragment order [G, K, N] and its block scales [G, K/128, N/128]."""
+    _dev(w_q, "w_q")
+    _dev(w_s, "w_s")
+    squeeze = w_q.dim() == 2
+    G, N, K = (1, *w_q.shape) if squeeze else tuple(w_q.shape)
+    wt_q = torch.empty((G, K, N), dtype=torch.uint8, device=w_q.device)
+    wt_s = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device=w_q.device)
+    _check("moe_pack_weights_transposed", _lib.load().moe_pack_weights_transposed(
+        _p(w_q), _p(w_s), G, N, K, _p(wt_q), _p(wt_s), _stream(w_q)))
+    return (wt_q[0], wt_s[0]) if squeeze else (wt_q, wt_s)
+
+
+def fp8_grouped_gemm_wgrad(a_t: torch.Tensor, a_ts: torch.Tensor, b_t: torch.Tensor, b_ts: torch.Tensor,
+                           padded: torch.Tensor, M: int, out: torch.Tensor | None = None, ue8m0: bool = False):
+    """out[g] = A_g^T-operand x B_g over group g's padded rows: a_t [Na, Mp], b_t [Nb, Mp] from
+    fp8_quant_128x1_grouped (same grouping, M rows before padding) -> fp32 [G, Na, Nb]."""
+    _dev(a_t, "a_t")
+    _dev(b_t, "b_t")
+    Na, ld = a_t.shape
+    Nb = b_t.shape[0]
+    G = padded.numel() - 1
+    if out is None:
+        out = torch.empty((G, Na, Nb), dtype=torch.float32, device=a_t.device)
+    _check("fp8_grouped_gemm_wgrad", _lib.load().fp8_grouped_gemm_wgrad(
+        _p(a_t), _p(a_ts), _p(b_t), _p(b_ts), _p(padded), G, M, Na, Nb, ld, _p(out), _fmt(ue8m0), _stream(a_t)))
     return out

@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoefp8.so")
+# The in-tree library; MOEFP8_LIB names another build of it (the host-sanitizer build of the CPU
+# checks).  There is no fallback: a missing library raises.
+LIB_PATH = os.environ.get("MOEFP8_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoefp8.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -22,7 +24,8 @@ MOE_EPI_STORE_F32, MOE_EPI_STORE_BF16, MOE_EPI_SWIGLU_QUANT, MOE_EPI_WEIGHTED_SC
 EXPORTED = ("moe_status_string", "moe_last_error", "fp8_quant_1x128", "fp8_quant_128x128", "moe_route",
             "moe_permute_workspace_size", "moe_permute", "moe_unpermute", "fp8_grouped_gemm_blockscaled",
             "moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_stages", "moe_pack_weights",
-            "fp8_rmsnorm_quant_1x128", "moe_bias_update", "moe_ffn_forward_noalloc")
+            "fp8_rmsnorm_quant_1x128", "moe_bias_update", "moe_ffn_forward_noalloc", "moe_padded_rows",
+            "fp8_quant_128x1_grouped", "moe_pack_weights_transposed", "fp8_grouped_gemm_wgrad")
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_FWD_STAGE_EVENTS = 6
 
@@ -77,6 +80,10 @@ def load() -> ctypes.CDLL:
                                        vp, vp, i, ctypes.POINTER(ctypes.c_void_p), i, vp]),
         "moe_ffn_forward_noalloc": (i, [vp, i, ctypes.POINTER(MoeCfgC), ctypes.POINTER(MoeWeightsC), vp, vp, vp, vp,
                                         i, vp]),
+        "moe_padded_rows": (sz, [i, i]),
+        "fp8_quant_128x1_grouped": (i, [vp, i, i, i, i, vp, i, vp, vp, i, vp, i, vp]),
+        "moe_pack_weights_transposed": (i, [vp, vp, i, i, i, vp, vp, vp]),
+        "fp8_grouped_gemm_wgrad": (i, [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -378,6 +378,70 @@ int moe_pack_weights(const uint8_t* src, int G, int N, int K, uint8_t* dst, void
   return ok();
 }
 
+size_t moe_padded_rows(int M, int G) {
+  if (M < 0 || G < 1 || G > 1024) return 0;
+  return ((size_t)(M + 127) / 128 + (size_t)G) * 128;
+}
+
+int fp8_quant_128x1_grouped(const void* x, int x_dtype, int M, int N, int ld_x, const int32_t* offsets, int G,
+                            int32_t* padded_offsets, uint8_t* q_t, int ld_q, float* s_t, int scale_fmt, void* stream) {
+  REQUIRE(x_dtype == MOE_DTYPE_BF16 || x_dtype == MOE_DTYPE_F32, MOE_ERR_INVALID_ARG, "x_dtype %d not BF16/F32",
+          x_dtype);
+  REQUIRE(scale_fmt == MOE_SCALE_F32 || scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG, "scale_fmt %d unknown",
+          scale_fmt);
+  REQUIRE(G >= 1 && G <= 1024, MOE_ERR_UNSUPPORTED_SHAPE, "G %d not in [1, 1024]", G);
+  REQUIRE(M >= 0 && M <= (1 << 30), MOE_ERR_INVALID_ARG, "M %d", M);
+  REQUIRE(N > 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "N %d not a positive multiple of 128", N);
+  REQUIRE(ld_x >= N, MOE_ERR_INVALID_ARG, "ld_x %d < N %d", ld_x, N);
+  const size_t mp = moe_padded_rows(M, G);
+  REQUIRE(ld_q % 128 == 0 && (size_t)ld_q >= mp, MOE_ERR_INVALID_ARG,
+          "ld_q %d: a multiple of 128 of at least moe_padded_rows(M, G) = %zu", ld_q, mp);
+  REQUIRE(x && offsets && padded_offsets && q_t && s_t, MOE_ERR_INVALID_ARG, "NULL pointer");
+  const int esz = x_dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  REQUIRE(aligned(x, 16) && ((size_t)ld_x * esz) % 16 == 0 && aligned(q_t, 16) && aligned(s_t, 4) &&
+              aligned(offsets, 4) && aligned(padded_offsets, 4),
+          MOE_ERR_INVALID_ARG, "pointer or leading dimension not aligned");
+  const hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(launch_pad_offsets(offsets, G, padded_offsets, st), "pad offsets");
+  HIP_TRY(launch_quant_128x1_grouped(x, x_dtype == MOE_DTYPE_BF16, ld_x, offsets, G, padded_offsets, (int)mp, N, q_t,
+                                     ld_q, s_t, scale_fmt == MOE_SCALE_UE8M0, st),
+          "fp8_quant_128x1_grouped");
+  return ok();
+}
+
+int moe_pack_weights_transposed(const uint8_t* w_q, const float* w_s, int G, int N, int K, uint8_t* wt_q, float* wt_s,
+                                void* stream) {
+  REQUIRE(G >= 0 && N >= 0 && K >= 0, MOE_ERR_INVALID_ARG, "negative size");
+  REQUIRE(N % 128 == 0 && K % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "N %d / K %d not multiples of 128", N, K);
+  if ((long)G * N * K == 0) return ok();
+  REQUIRE(w_q && w_s && wt_q && wt_s && w_q != wt_q, MOE_ERR_INVALID_ARG, "NULL or aliased pointers");
+  REQUIRE(aligned(w_q, 16) && aligned(wt_q, 16) && aligned(w_s, 4) && aligned(wt_s, 4), MOE_ERR_INVALID_ARG,
+          "pointer not aligned");
+  HIP_TRY(launch_pack_transposed(w_q, w_s, G, N, K, wt_q, wt_s, (hipStream_t)stream), "moe_pack_weights_transposed");
+  return ok();
+}
+
+int fp8_grouped_gemm_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_t, const float* b_ts,
+                           const int32_t* padded_offsets, int G, int M, int Na, int Nb, int ld, float* out,
+                           int scale_fmt, void* stream) {
+  REQUIRE(scale_fmt == MOE_SCALE_F32 || scale_fmt == MOE_SCALE_UE8M0, MOE_ERR_INVALID_ARG, "scale_fmt %d unknown",
+          scale_fmt);
+  REQUIRE(G >= 1 && G <= 1024, MOE_ERR_UNSUPPORTED_SHAPE, "G %d not in [1, 1024]", G);
+  REQUIRE(M >= 0 && M <= (1 << 30), MOE_ERR_INVALID_ARG, "M %d", M);
+  REQUIRE(Na > 0 && Nb > 0 && Na % 128 == 0 && Nb % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE,
+          "Na %d / Nb %d not positive multiples of 128", Na, Nb);
+  const size_t mp = moe_padded_rows(M, G);
+  REQUIRE(ld % 128 == 0 && (size_t)ld >= mp, MOE_ERR_INVALID_ARG,
+          "ld %d: a multiple of 128 of at least moe_padded_rows(M, G) = %zu", ld, mp);
+  REQUIRE(a_t && a_ts && b_t && b_ts && padded_offsets && out, MOE_ERR_INVALID_ARG, "NULL pointer");
+  REQUIRE(aligned(a_t, 16) && aligned(b_t, 16) && aligned(out, 16) && aligned(a_ts, 4) && aligned(b_ts, 4),
+          MOE_ERR_INVALID_ARG, "pointer not aligned");
+  HIP_TRY(launch_wgrad(a_t, a_ts, b_t, b_ts, padded_offsets, G, Na, Nb, ld, out, scale_fmt == MOE_SCALE_UE8M0,
+                       (hipStream_t)stream),
+          "fp8_grouped_gemm_wgrad");
+  return ok();
+}
+
 size_t moe_ffn_workspace_size(int T, const moe_cfg_t* cfg) {
   if (T < 0 || check_layer_cfg(cfg) != MOE_OK) return 0;
   return fwd_layout(T, cfg).total;

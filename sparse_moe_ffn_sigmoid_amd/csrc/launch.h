@@ -63,6 +63,16 @@ hipError_t launch_unpermute(const void* y, const int32_t* ap, long n, int row_by
 hipError_t launch_cast_bf16(const float* in, long n, uint16_t* out, hipStream_t st);
 hipError_t launch_fill_zero(float* p, long n, hipStream_t st);
 
+// FP8 backward (backward.hip).
+hipError_t launch_pad_offsets(const int32_t* offsets, int G, int32_t* padded, hipStream_t st);
+hipError_t launch_quant_128x1_grouped(const void* x, bool bf16, int ld_x, const int32_t* offsets, int G,
+                                      const int32_t* padded, int M_pad_max, int N, uint8_t* qt, int ld_q, float* st,
+                                      bool pow2, hipStream_t s);
+hipError_t launch_pack_transposed(const uint8_t* src, const float* s, int G, int N, int K, uint8_t* dst, float* s_t,
+                                  hipStream_t st);
+hipError_t launch_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_t, const float* b_ts,
+                        const int32_t* padded, int G, int Na, int Nb, int ld, float* out, bool pow2, hipStream_t st);
+
 // Grouped block-scaled GEMM.  bm = rows per tile (16, 32, 64 or 128); the
 // caller sets each segment's m_tiles for that bm.
 hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st);

@@ -1,6 +1,6 @@
 """moe_ffn_forward_noalloc (workspace in the library's static device array) against
-moe_ffn_forward (caller workspace): the same launches, so outputs and routing must agree bit
-for bit; two calls in a row, the second on a smaller batch, since the array keeps the previous
+moe_ffn_forward (caller workspace): the same launches with the slot-ordered combine
+(MOE_FWD_DETERMINISTIC), so outputs and routing must agree bit for bit; two calls in a row, the second on a smaller batch, since the array keeps the previous
 call's contents.  Sizes beyond the array are rejected on the host."""
 import numpy as np
 import pytest
@@ -26,7 +26,7 @@ def _both(layer, xb):
         ti = torch.full((T, s.top_k), -1, dtype=torch.int32, device=DEV)
         tw = torch.full((T, s.top_k), -1.0, dtype=torch.float32, device=DEV)
         sc = torch.zeros((T, s.n_experts), dtype=torch.float32, device=DEV)
-        out = fn(x, layer.cfg, layer.weights, scores=sc, topk_idx=ti, topk_w=tw)
+        out = fn(x, layer.cfg, layer.weights, scores=sc, topk_idx=ti, topk_w=tw, deterministic=True)
         torch.cuda.synchronize()
         res.append([out.float().cpu().numpy(), ti.cpu().numpy(), tw.cpu().numpy(), sc.cpu().numpy()])
     return res
