@@ -573,7 +573,9 @@ def time_workload(shape, steps: int, warmup: int, ue8m0: bool = False, rmsnorm: 
     else:
         roof = {"bound": "mfma", "achieved": gate_up_flops / t_gu / 1e12, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(shape) if not (ue8m0 or rmsnorm) else None   # counted on the default
+    # counted on the default scale format, at the workload's own size
+    counted = not (ue8m0 or rmsnorm) and shape == synth.SHAPES[shape.name]
+    roof["traffic"] = stored_traffic(shape) if counted else None
     roof["kernel"] = gate_up_kernel(shape, ue8m0) + " (gate/up GEMM, SwiGLU + requantisation epilogue)"
     roof["avg_ms"] = stage["gate_up_gemm"]
     # the other bound, for the record: the gate/up GEMM's FLOP rate or its algorithmic byte rate
@@ -689,6 +691,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_decode")
+    ap.add_argument("--tokens", type=int, help="run the workload's layer at this many tokens instead (a batch-size "
+                                                "sweep; the line's config records it)")
     ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens of the workload the CPU oracle runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
@@ -724,6 +728,8 @@ def main():
 
     import synth
     shape = synth.SHAPES[args.workload]
+    if args.tokens:
+        shape = synth.with_tokens(shape, args.tokens)
     if args.backward:
         print(json.dumps({"workload": shape.name, "backward": time_backward(shape, args.steps, args.warmup)}))
         return
@@ -733,7 +739,7 @@ def main():
            "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic"}
     res.update({k: v for k, v in rec.items() if k not in res and k not in ("steps", "warmup")})
-    if shape.name == "v3_decode" and not args.no_prefill:
+    if shape == synth.V3_DECODE and not args.no_prefill:
         # the MFMA half of the metric: the V3 prefill step (T = 4096) timed the same way
         sub, _ = time_workload(synth.V3_PREFILL, max(5, args.steps // 2), max(2, args.warmup), ue8m0=args.ue8m0,
                                rmsnorm=args.rmsnorm, deterministic=args.deterministic, with_next_rows=False)

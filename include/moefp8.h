@@ -24,8 +24,18 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work and return; nothing synchronises the host.
  *   - Shapes and pointers are checked on the host before anything is enqueued;
- *     a failed check enqueues nothing.  Device data (expert ids, offsets) is
- *     trusted: out-of-range ids are undefined behaviour.
+ *     a failed check enqueues nothing.
+ *   - Device data (expert ids, positions, offsets, given scores) is trusted by
+ *     default: values that break a call's stated contract give undefined results
+ *     and may fault the GPU.  With the environment variable MOEFP8_VALIDATE set
+ *     (to anything but "" or "0") when a call is made, the calls that read such
+ *     data check it on the device first, synchronise `stream`, and return
+ *     MOE_ERR_INVALID_DATA, enqueuing nothing else, when an element breaks the
+ *     contract (the message names the first such element and its value).  What
+ *     each call checks is listed with it ("Validated:").  The checks cost one pass
+ *     over the data and a stream synchronisation per call (not usable under HIP
+ *     graph capture); their result word is one per GPU, so validated calls that
+ *     overlap on one GPU (other streams or threads) race on it.
  *   - Layouts are row-major.  FP8 means OCP E4M3FN bytes (max 448, no inf,
  *     0x7F/0xFF NaN).  bf16 and fp8 data are passed as raw bits.
  *   - Alignment: every pointer 16-byte aligned; leading dimensions keep rows
@@ -53,6 +63,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED_SHAPE (-2) /* a size the kernels do not handle (e.g. not % 128)     */
 #define MOE_ERR_WORKSPACE (-3)         /* workspace missing or smaller than required            */
 #define MOE_ERR_HIP (-4)               /* a HIP launch failed (hipGetLastError after enqueue)   */
+#define MOE_ERR_INVALID_DATA (-5)      /* MOEFP8_VALIDATE: device data breaks the call's contract */
 
 /* ---- element types ---- */
 #define MOE_DTYPE_F32 0
@@ -132,6 +143,8 @@ typedef struct moe_epi {
 
 MOE_API const char* moe_status_string(int status);
 MOE_API const char* moe_last_error(void);
+/* moe_validation_enabled - 1 when calls made now validate device data (MOEFP8_VALIDATE), else 0. */
+MOE_API int moe_validation_enabled(void);
 
 /* fp8_quant_1x128 - online activation quantisation ([arch blog] "Fine granularity
  * quantization", "Online Quantization").  Per row, per 128 consecutive columns:
@@ -189,7 +202,8 @@ MOE_API int moe_pack_weights(const uint8_t* src, int G, int N, int K, uint8_t* d
  *   x bf16 [T][hidden] or NULL; w_router bf16 [E][hidden] or NULL; bias f32 [E] or NULL;
  *   scores f32 [T][E] (in or out); topk_idx i32 [T][top_k]; topk_w f32 [T][top_k].
  * Requires n_experts % n_group == 0, topk_group <= n_group, top_k <= topk_group *
- * n_experts / n_group, n_experts <= 1024, n_group <= 64, top_k <= 64.          */
+ * n_experts / n_group, n_experts <= 1024, n_group <= 64, top_k <= 64.
+ * Validated: given scores and bias finite (NaN scores route arbitrarily).      */
 MOE_API int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, const moe_cfg_t* cfg,
               float* scores, int flags, int32_t* topk_idx, float* topk_w, void* stream);
 
@@ -210,7 +224,8 @@ MOE_API int moe_bias_update(const int32_t* topk_idx, int T, int k, int E, float 
  * Optionally gathers rows: rows_out[p] = rows_in[sorted_assign[p] / k]
  * (row_bytes each, a multiple of 16; pass NULL for both to skip).
  *   topk_idx i32 [T][k]; offsets i32 [E+1]; sorted_assign, assign_pos i32 [T*k].
- * Scratch: the call needs moe_permute_workspace_size(T, k, E) bytes in `ws`. */
+ * Scratch: the call needs moe_permute_workspace_size(T, k, E) bytes in `ws`.
+ * Validated: every topk_idx entry in [0, E).                                 */
 MOE_API size_t moe_permute_workspace_size(int T, int k, int E);
 MOE_API int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* offsets, int32_t* sorted_assign,
                 int32_t* assign_pos, const void* rows_in, int row_bytes, void* rows_out, void* ws,
@@ -222,7 +237,8 @@ MOE_API int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* o
  *   topk_w != NULL (y_dtype F32): out bf16 [T][d] =
  *     bf16(sum_j topk_w[t][j] * y_sorted[assign_pos[t*k+j]] + shared_y[t]),
  *     summed in fp32 in slot order, shared_y f32 [T][d] or NULL (shared weight 1,
- *     [arch blog] "Structural change").  d % 4 == 0.                          */
+ *     [arch blog] "Structural change").  d % 4 == 0, T*k <= 2^30.
+ * Validated: every assign_pos entry in [0, T*k).                            */
 MOE_API int moe_unpermute(const void* y_sorted, int y_dtype, const int32_t* assign_pos, const float* topk_w,
                   const float* shared_y, int T, int k, int d, void* out, void* stream);
 
@@ -236,7 +252,10 @@ MOE_API int moe_unpermute(const void* y_sorted, int y_dtype, const int32_t* assi
  *   M_max: an upper bound of offsets[G] known on the host (sizes the launch).
  *   epilogue MOE_EPI_* with `out` and `epi` as documented at the constants.
  * N % 128 == 0 (SWIGLU_QUANT: N % 256 == 0), K % 128 == 0, G >= 1.  G = 1 with
- * offsets {0, M} is a plain block-scaled GEMM (the dense layer).            */
+ * offsets {0, M} is a plain block-scaled GEMM (the dense layer).
+ * Validated: 0 <= offsets[0] <= ... <= offsets[G] <= M_max; a_gather[m] >= 0 and
+ * (WEIGHTED_SCATTER_ADD) epi->dst_row[m] >= 0 for the rows m of the groups (the
+ * arrays' row counts are not known to the call).                            */
 MOE_API int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int32_t* a_gather, const uint8_t* b_q,
                                  const float* b_s, const int32_t* offsets, int G, int M_max, int N, int K,
                                  int epilogue, const moe_epi_t* epi, void* out, void* stream);
@@ -259,7 +278,8 @@ MOE_API size_t moe_ffn_workspace_size(int T, const moe_cfg_t* cfg);
  *   (NULL to skip); with MOE_ROUTE_SCORES_GIVEN `scores` is an input instead.
  *   The combine is slot-ordered in fp32, so the output is bit-reproducible run to
  *   run (MOE_FWD_DETERMINISTIC is accepted and changes nothing).
- * ws: at least moe_ffn_workspace_size(T, cfg) bytes, 256-byte aligned.     */
+ * ws: at least moe_ffn_workspace_size(T, cfg) bytes, 256-byte aligned.
+ * Validated (routed layers): given scores and the routing bias finite.      */
 MOE_API int moe_ffn_forward(const uint16_t* x, int T, const moe_cfg_t* cfg, const moe_weights_t* w, void* ws,
                     size_t ws_bytes, uint16_t* out, float* scores, int32_t* topk_idx, float* topk_w, int flags,
                     void* stream);
@@ -300,7 +320,8 @@ MOE_API size_t moe_padded_rows(int M, int G);
  * with q_t[n][padded[g] + r] the code of x[offsets[g] + r][n] (zeros in a group's padding),
  * s_t f32 [N][ld_q / 128], one scale per column and 128 padded rows, by the rule of
  * fp8_quant_1x128.  N % 128 == 0; ld_q % 128 == 0 and ld_q >= moe_padded_rows(M, G) (columns
- * past padded[G] are not written).  1 <= G <= 1024.                                      */
+ * past padded[G] are not written).  1 <= G <= 1024.
+ * Validated: 0 = offsets[0] <= ... <= offsets[G] = M.                                    */
 MOE_API int fp8_quant_128x1_grouped(const void* x, int x_dtype, int M, int N, int ld_x, const int32_t* offsets,
                                     int G, int32_t* padded_offsets, uint8_t* q_t, int ld_q, float* s_t,
                                     int scale_fmt, void* stream);
@@ -319,7 +340,8 @@ MOE_API int moe_pack_weights_transposed(const uint8_t* w_q, const float* w_s, in
  * operands).  a_t e4m3 [Na][ld], a_ts f32 [Na][ld/128], b_t e4m3 [Nb][ld], b_ts f32
  * [Nb][ld/128] (from fp8_quant_128x1_grouped); padded_offsets i32 [G+1] (device); M the rows
  * before padding (bounds the padded rows); out f32 [G][Na][Nb] (a group without rows gets
- * zeros).  Na % 128 == 0, Nb % 128 == 0, ld as for fp8_quant_128x1_grouped.               */
+ * zeros).  Na % 128 == 0, Nb % 128 == 0, ld as for fp8_quant_128x1_grouped.
+ * Validated: 0 = padded[0] <= ... <= padded[G] <= moe_padded_rows(M, G), multiples of 128. */
 MOE_API int fp8_grouped_gemm_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_t, const float* b_ts,
                                    const int32_t* padded_offsets, int G, int M, int Na, int Nb, int ld, float* out,
                                    int scale_fmt, void* stream);

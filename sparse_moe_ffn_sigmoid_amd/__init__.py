@@ -9,7 +9,11 @@ Calls (same names as the C ABI in include/moefp8.h):
     fp8_quant_1x128, fp8_quant_128x128, fp8_rmsnorm_quant_1x128, moe_pack_weights, moe_route,
     moe_bias_update, moe_permute, moe_unpermute, fp8_grouped_gemm_blockscaled, moe_ffn_workspace_size,
     moe_ffn_forward, moe_ffn_forward_noalloc, moe_padded_rows, fp8_quant_128x1_grouped,
-    moe_pack_weights_transposed, fp8_grouped_gemm_wgrad
+    moe_pack_weights_transposed, fp8_grouped_gemm_wgrad, moe_validation_enabled
+
+With MOEFP8_VALIDATE set in the environment, the calls check the device data they read (ids,
+positions, offsets, given scores) before launching and raise MoeError with status
+MOE_ERR_INVALID_DATA when an element breaks the call's contract.
 """
 from __future__ import annotations
 
@@ -19,7 +23,7 @@ import dataclasses
 import torch
 
 from . import _lib
-from ._lib import (MOE_EPI_STORE_BF16, MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_QUANT,  # noqa: F401
+from ._lib import (MOE_ERR_INVALID_DATA, MOE_EPI_STORE_BF16, MOE_EPI_STORE_F32, MOE_EPI_SWIGLU_QUANT,  # noqa: F401
                    MOE_EPI_WEIGHTED_SCATTER_ADD, MOE_FWD_DETERMINISTIC, MOE_GROUP_SCORE_MAX,
                    MOE_GROUP_SCORE_TOP2_SUM, MOE_ROUTE_SCORES_GIVEN, MOE_SCALE_F32, MOE_SCALE_UE8M0)
 
@@ -312,6 +316,11 @@ def moe_ffn_forward_noalloc(x: torch.Tensor, cfg: MoeConfig, weights: MoeWeights
         _p(x), T, ctypes.byref(c), ctypes.byref(wc), _p(out), _p(scores), _p(topk_idx), _p(topk_w), flags,
         _stream(x)))
     return out
+
+
+def moe_validation_enabled() -> bool:
+    """Whether calls made now check their device data first (MOEFP8_VALIDATE, read per call)."""
+    return bool(_lib.load().moe_validation_enabled())
 
 
 # ---- FP8 backward of the grouped GEMMs ----

@@ -13,6 +13,7 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED_SHAPE = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_INVALID_DATA = -5
 
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_U8 = 0, 1, 2
 MOE_SCALE_F32, MOE_SCALE_UE8M0 = 0, 1
@@ -25,7 +26,8 @@ EXPORTED = ("moe_status_string", "moe_last_error", "fp8_quant_1x128", "fp8_quant
             "moe_permute_workspace_size", "moe_permute", "moe_unpermute", "fp8_grouped_gemm_blockscaled",
             "moe_ffn_workspace_size", "moe_ffn_forward", "moe_ffn_forward_stages", "moe_pack_weights",
             "fp8_rmsnorm_quant_1x128", "moe_bias_update", "moe_ffn_forward_noalloc", "moe_padded_rows",
-            "fp8_quant_128x1_grouped", "moe_pack_weights_transposed", "fp8_grouped_gemm_wgrad")
+            "fp8_quant_128x1_grouped", "moe_pack_weights_transposed", "fp8_grouped_gemm_wgrad",
+            "moe_validation_enabled")
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_FWD_STAGE_EVENTS = 6
 
@@ -63,6 +65,7 @@ def load() -> ctypes.CDLL:
     sig = {
         "moe_status_string": (ctypes.c_char_p, [i]),
         "moe_last_error": (ctypes.c_char_p, []),
+        "moe_validation_enabled": (i, []),
         "fp8_quant_1x128": (i, [vp, i, i, i, i, vp, i, vp, i, vp]),
         "fp8_quant_128x128": (i, [vp, i, i, vp, vp, i, vp]),
         "fp8_rmsnorm_quant_1x128": (i, [vp, vp, ctypes.c_float, i, i, i, vp, i, vp, i, vp, i, vp]),

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoefp8.so")
-SOURCES = ["quant.hip", "route.hip", "permute.hip", "gemm.hip", "backward.hip", "api.hip"]
+SOURCES = ["quant.hip", "route.hip", "permute.hip", "gemm.hip", "backward.hip", "validate.hip", "api.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -3,6 +3,8 @@
 // returns a status; launches are asynchronous on the caller's stream.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
 
@@ -52,6 +54,32 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
   do {                                            \
     const int st_ = hip_check((expr), (what));    \
     if (st_ != MOE_OK) return st_;                \
+  } while (0)
+
+// MOEFP8_VALIDATE, read at each call: set to anything but "" or "0", the calls check the device
+// data they would otherwise trust (validate.hip) before enqueueing their own kernels.
+bool validation_on() {
+  const char* e = std::getenv("MOEFP8_VALIDATE");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+// One element of a device array, for the message of a failed check (the stream is synchronised).
+long read_i32(const int32_t* p, long i) {
+  int32_t v = 0;
+  return hipMemcpy(&v, p + i, sizeof(v), hipMemcpyDeviceToHost) == hipSuccess ? (long)v : -999999999L;
+}
+double read_f32(const float* p, long i) {
+  float v = 0.0f;
+  return hipMemcpy(&v, p + i, sizeof(v), hipMemcpyDeviceToHost) == hipSuccess ? (double)v : 0.0;
+}
+
+// Runs a validate_* check (it sets bad_) and returns MOE_ERR_INVALID_DATA with the message when
+// an element fails.
+#define VALIDATE(check, ...)                                                   \
+  do {                                                                         \
+    long bad_ = -1;                                                            \
+    HIP_TRY((check), "MOEFP8_VALIDATE check");                                 \
+    if (bad_ >= 0) return fail(MOE_ERR_INVALID_DATA, "MOEFP8_VALIDATE: " __VA_ARGS__); \
   } while (0)
 
 // Routing configuration checks shared by moe_route and moe_ffn_forward.
@@ -170,11 +198,14 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_INVALID_DATA: return "MOE_ERR_INVALID_DATA";
     default: return "MOE_ERR_UNKNOWN";
   }
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_validation_enabled(void) { return validation_on() ? 1 : 0; }
 
 int fp8_quant_1x128(const void* x, int x_dtype, int rows, int cols, int ld_x, uint8_t* q, int ld_q, float* s,
                     int scale_fmt, void* stream) {
@@ -253,6 +284,14 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, in
   if (T == 0) return ok();
   REQUIRE(scores && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "NULL scores/topk_idx/topk_w");
   const hipStream_t s = (hipStream_t)stream;
+  if (validation_on()) {
+    if (flags & MOE_ROUTE_SCORES_GIVEN)
+      VALIDATE(validate_finite(scores, (long)T * cfg->n_experts, s, &bad_), "scores[%ld] = %g is not finite", bad_,
+               read_f32(scores, bad_));
+    if (bias)
+      VALIDATE(validate_finite(bias, cfg->n_experts, s, &bad_), "bias[%ld] = %g is not finite", bad_,
+               read_f32(bias, bad_));
+  }
   if (!(flags & MOE_ROUTE_SCORES_GIVEN)) {
     REQUIRE(x && w_router, MOE_ERR_INVALID_ARG, "x and w_router are needed unless MOE_ROUTE_SCORES_GIVEN");
     REQUIRE(cfg->hidden > 0 && cfg->hidden % 128 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "hidden %d not a multiple of 128",
@@ -289,6 +328,9 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* offsets, 
   const size_t need = moe_permute_workspace_size(T, k, E);
   REQUIRE(need == 0 || (ws && ws_bytes >= need), MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   const hipStream_t s = (hipStream_t)stream;
+  if (validation_on() && T > 0)
+    VALIDATE(validate_range(topk_idx, T * k, 0, E, s, &bad_), "topk_idx[%ld] = %ld not in [0, %d)", bad_,
+             read_i32(topk_idx, bad_), E);
   HIP_TRY(launch_permute(topk_idx, T, k, E, offsets, sorted_assign, assign_pos, nullptr, nullptr, nullptr,
                          reinterpret_cast<int32_t*>(ws), s),
           "moe_permute");
@@ -302,11 +344,15 @@ int moe_unpermute(const void* y_sorted, int y_dtype, const int32_t* assign_pos, 
   REQUIRE(y_dtype == MOE_DTYPE_F32 || y_dtype == MOE_DTYPE_BF16 || y_dtype == MOE_DTYPE_U8, MOE_ERR_INVALID_ARG,
           "y_dtype %d unknown", y_dtype);
   REQUIRE(d % 4 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "d %d not a multiple of 4", d);
+  REQUIRE((long)T * k <= (1l << 30), MOE_ERR_UNSUPPORTED_SHAPE, "T*k too large");
   if (T == 0) return ok();
   REQUIRE(y_sorted && assign_pos && out, MOE_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned(y_sorted, 16) && aligned(out, 16) && (!shared_y || aligned(shared_y, 16)), MOE_ERR_INVALID_ARG,
           "pointer not 16-byte aligned");
   const hipStream_t s = (hipStream_t)stream;
+  if (validation_on())
+    VALIDATE(validate_range(assign_pos, T * k, 0, T * k, s, &bad_), "assign_pos[%ld] = %ld not in [0, %d)", bad_,
+             read_i32(assign_pos, bad_), T * k);
   if (topk_w) {
     REQUIRE(y_dtype == MOE_DTYPE_F32, MOE_ERR_INVALID_ARG, "the weighted combine takes F32 rows");
     HIP_TRY(launch_combine(reinterpret_cast<const float*>(y_sorted), assign_pos, topk_w, shared_y, T, k, d,
@@ -332,6 +378,18 @@ int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int
   if (M_max == 0) return ok();
   REQUIRE(a_q && a_s && b_q && b_s && offsets && out, MOE_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned(a_q, 16) && aligned(b_q, 16) && aligned(out, 16), MOE_ERR_INVALID_ARG, "pointer not 16-byte aligned");
+  if (validation_on()) {
+    const hipStream_t s = (hipStream_t)stream;
+    VALIDATE(validate_offsets(offsets, G, -1, M_max, false, 1, s, &bad_),
+             "offsets[%ld] = %ld breaks 0 <= offsets[0] <= ... <= offsets[G] <= M_max = %d", bad_,
+             read_i32(offsets, bad_), M_max);
+    if (a_gather)
+      VALIDATE(validate_rows(a_gather, offsets, G, M_max, s, &bad_), "a_gather[%ld] = %ld < 0", bad_,
+               read_i32(a_gather, bad_));
+    if (epilogue == MOE_EPI_WEIGHTED_SCATTER_ADD && epi && epi->dst_row)
+      VALIDATE(validate_rows(epi->dst_row, offsets, G, M_max, s, &bad_), "epi->dst_row[%ld] = %ld < 0", bad_,
+               read_i32(epi->dst_row, bad_));
+  }
   GemmArgs args{};
   GemmSeg& sg = args.seg[1];
   const int bm = gemm_pick_bm(M_max, G);
@@ -402,6 +460,10 @@ int fp8_quant_128x1_grouped(const void* x, int x_dtype, int M, int N, int ld_x, 
               aligned(offsets, 4) && aligned(padded_offsets, 4),
           MOE_ERR_INVALID_ARG, "pointer or leading dimension not aligned");
   const hipStream_t st = (hipStream_t)stream;
+  if (validation_on())
+    VALIDATE(validate_offsets(offsets, G, 0, M, true, 1, st, &bad_),
+             "offsets[%ld] = %ld breaks 0 = offsets[0] <= ... <= offsets[G] = M = %d", bad_, read_i32(offsets, bad_),
+             M);
   HIP_TRY(launch_pad_offsets(offsets, G, padded_offsets, st), "pad offsets");
   HIP_TRY(launch_quant_128x1_grouped(x, x_dtype == MOE_DTYPE_BF16, ld_x, offsets, G, padded_offsets, (int)mp, N, q_t,
                                      ld_q, s_t, scale_fmt == MOE_SCALE_UE8M0, st),
@@ -436,6 +498,10 @@ int fp8_grouped_gemm_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t*
   REQUIRE(a_t && a_ts && b_t && b_ts && padded_offsets && out, MOE_ERR_INVALID_ARG, "NULL pointer");
   REQUIRE(aligned(a_t, 16) && aligned(b_t, 16) && aligned(out, 16) && aligned(a_ts, 4) && aligned(b_ts, 4),
           MOE_ERR_INVALID_ARG, "pointer not aligned");
+  if (validation_on())
+    VALIDATE(validate_offsets(padded_offsets, G, 0, (int)mp, false, 128, (hipStream_t)stream, &bad_),
+             "padded_offsets[%ld] = %ld breaks 0 = padded[0] <= ... <= padded[G] <= moe_padded_rows(M, G) = %zu "
+             "in multiples of 128", bad_, read_i32(padded_offsets, bad_), mp);
   HIP_TRY(launch_wgrad(a_t, a_ts, b_t, b_ts, padded_offsets, G, Na, Nb, ld, out, scale_fmt == MOE_SCALE_UE8M0,
                        (hipStream_t)stream),
           "fp8_grouped_gemm_wgrad");
@@ -499,6 +565,14 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
           "workspace %zu bytes (needs %zu, 256-byte aligned)", ws_bytes, L.total);
 
   const hipStream_t s = (hipStream_t)stream;
+  if (validation_on() && routed) {
+    if (flags & MOE_ROUTE_SCORES_GIVEN)
+      VALIDATE(validate_finite(scores, (long)T * cfg->n_experts, s, &bad_), "scores[%ld] = %g is not finite", bad_,
+               read_f32(scores, bad_));
+    if (w->bias)
+      VALIDATE(validate_finite(w->bias, cfg->n_experts, s, &bad_), "bias[%ld] = %g is not finite", bad_,
+               read_f32(w->bias, bad_));
+  }
   auto mark = [&](int i) -> hipError_t {
     return n_events && events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };

@@ -78,4 +78,18 @@ hipError_t launch_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_
 hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st);
 int gemm_pick_bm(long rows_upper, int groups);
 
+// Device-data checks (validate.hip).  Each runs on `st`, synchronises it and sets *first_bad to
+// the smallest offending element index, or -1 when every element passes.
+//   validate_range:   v[i] in [lo, hi) for i < n
+//   validate_offsets: off[0..G] nondecreasing multiples of align, off[0] == first (first < 0:
+//                     off[0] >= 0), off[G] <= last (== last when last_exact)
+//   validate_rows:    idx[m] >= 0 for off[0] <= m < off[G] (off already validated; max_rows
+//                     bounds off[G])
+//   validate_finite:  v[i] neither NaN nor infinite for i < n
+hipError_t validate_range(const int32_t* v, int n, int lo, int hi, hipStream_t st, long* first_bad);
+hipError_t validate_offsets(const int32_t* off, int G, int first, int last, bool last_exact, int align, hipStream_t st,
+                            long* first_bad);
+hipError_t validate_rows(const int32_t* idx, const int32_t* off, int G, int max_rows, hipStream_t st, long* first_bad);
+hipError_t validate_finite(const float* v, long n, hipStream_t st, long* first_bad);
+
 }  // namespace moefp8

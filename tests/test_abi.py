@@ -184,3 +184,71 @@ def test_forward_checks(lib):
     wn = _lib.MoeWeightsC(*([0x10000] * 10 + [0x10008]))                                    # norm_w misaligned
     assert lib.moe_ffn_forward(FAKE, 64, ctypes.byref(c), ctypes.byref(wn), FAKE, need, FAKE, None, None, None, 0,
                                None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_invalid_data_status_and_switch(lib, monkeypatch):
+    assert lib.moe_status_string(_lib.MOE_ERR_INVALID_DATA) == b"MOE_ERR_INVALID_DATA"
+    for val, on in ((None, 0), ("", 0), ("0", 0), ("1", 1), ("yes", 1)):
+        if val is None:
+            monkeypatch.delenv("MOEFP8_VALIDATE", raising=False)
+        else:
+            monkeypatch.setenv("MOEFP8_VALIDATE", val)
+        assert lib.moe_validation_enabled() == on, val
+
+
+# Calls whose arguments pass the host checks, so that each reaches its first device step.  They run
+# in a child process that sees no GPU (HIP_VISIBLE_DEVICES=-1), where that step fails with
+# MOE_ERR_HIP and the message names it: the validation check with MOEFP8_VALIDATE set, the call's
+# own launch without.  Nothing runs on a device (the child exits early if one is visible anyway).
+_PLUMBING = r'''
+import ctypes, os, sys
+n = ctypes.c_int(0)
+if ctypes.CDLL("libamdhip64.so").hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0:
+    print("SKIP a device is visible"); sys.exit(0)
+from sparse_moe_ffn_sigmoid_amd import _lib
+lib = _lib.load()
+F = ctypes.c_void_p(0x100000)
+def cfg(**kw):
+    base = dict(hidden=7168, inter=2048, n_experts=256, top_k=8, n_shared=1, inter_shared=2048, n_group=8,
+                topk_group=4, group_score=0, routed_scale=1.0, scale_fmt=0, norm_eps=1e-6)
+    base.update(kw)
+    return _lib.MoeCfgC(**base)
+c = cfg()
+w = _lib.MoeWeightsC(*([0x100000] * 10))
+epi = _lib.MoeEpiC(None, F.value, None, 0)
+need = lib.moe_ffn_workspace_size(64, ctypes.byref(c))
+calls = {
+    "moe_permute": lambda: lib.moe_permute(F, 4, 2, 8, F, F, F, None, 0, None, F, 1 << 20, None),
+    "moe_unpermute": lambda: lib.moe_unpermute(F, 0, F, None, None, 4, 2, 16, F, None),
+    "fp8_grouped_gemm_blockscaled": lambda: lib.fp8_grouped_gemm_blockscaled(
+        F, F, F, F, F, F, 4, 64, 256, 128, 3, ctypes.byref(epi), F, None),
+    "fp8_quant_128x1_grouped": lambda: lib.fp8_quant_128x1_grouped(F, 1, 64, 128, 128, F, 2, F, F, 384, F, 0, None),
+    "fp8_grouped_gemm_wgrad": lambda: lib.fp8_grouped_gemm_wgrad(F, F, F, F, F, 2, 64, 128, 128, 384, F, 0, None),
+    "moe_route": lambda: lib.moe_route(None, None, F, 4, ctypes.byref(c), F, 1, F, F, None),
+    "moe_ffn_forward": lambda: lib.moe_ffn_forward(F, 64, ctypes.byref(c), ctypes.byref(w), F, need, F, F, None,
+                                                   None, 1, None),
+}
+for name, call in calls.items():
+    for val in ("1", "0"):
+        os.environ["MOEFP8_VALIDATE"] = val
+        st = call()
+        print(name, val, st, lib.moe_last_error().decode())
+'''
+
+
+def test_validation_runs_before_the_launches():
+    import subprocess
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", _PLUMBING], env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    if r.stdout.startswith("SKIP"):
+        pytest.skip("a GPU is visible to the child process")
+    rows = [ln.split(" ", 3) for ln in r.stdout.strip().splitlines()]
+    assert len(rows) == 14, r.stdout
+    for name, val, st, msg in rows:
+        assert int(st) == _lib.MOE_ERR_HIP, (name, val, st, msg)
+        if val == "1":
+            assert msg.startswith("MOEFP8_VALIDATE check"), (name, msg)
+        else:
+            assert not msg.startswith("MOEFP8_VALIDATE"), (name, msg)
