@@ -37,18 +37,20 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
   if (t == 0) padded[0] = 0;
 }
 
-// One workgroup per (128-row tile of the padded rows, 128 columns).  The tile's rows come from
-// one group (rows past the group's end are zeros); they are staged transposed in LDS (fp32,
-// rows padded by one word: conflict-free both ways), then thread t takes column t / 2, rows
-// (t % 2) * 64 .. +63: the column's amax over the two halves, its scale, and 64 codes written
-// as 64 contiguous bytes of the transposed output.
+// One workgroup per (128-row tile of the padded rows, 64 columns).  The tile's rows come from
+// one group (rows past the group's end are zeros).  Each wave loads 32 rows with 16-byte loads,
+// all in flight together, and stages them transposed in LDS (fp32, rows padded by one word;
+// 33 KB, so four workgroups share a CU); then thread t takes column t / 4, rows (t % 4) * 32 ..
+// +31: the column's amax over the four quarters (lane shuffles), its scale, and 32 codes written
+// as 32 contiguous bytes of the transposed output.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void quant_128x1_grouped_kernel(const void* __restrict__ x, int ld_x,
                                                                   const int32_t* __restrict__ offsets, int G,
                                                                   const int32_t* __restrict__ padded, int N,
                                                                   uint8_t* __restrict__ qt, int ld_q,
                                                                   float* __restrict__ st, int pow2) {
-  __shared__ float tile[128][129];
+  constexpr int kCols = 64;
+  __shared__ float tile[kCols][129];
   const int tid = threadIdx.x;
   const int p0 = blockIdx.x * 128;               // first padded row of the tile
   if (p0 >= padded[G]) return;
@@ -62,47 +64,61 @@ __global__ __launch_bounds__(256) void quant_128x1_grouped_kernel(const void* __
   const int g = lo;
   const int r0 = offsets[g] + (p0 - padded[g]);  // first source row
   const int rows = min(128, offsets[g + 1] - r0);
-  const int c0 = blockIdx.y * 128;
-  // load: 4 waves x 1 row per step; lane l takes columns 2l, 2l + 1
+  const int c0 = blockIdx.y * kCols;
   const int wave = tid >> 6, lane = tid & 63;
-  for (int r = wave; r < 128; r += 4) {
-    float a = 0.0f, b = 0.0f;
+  // load: a 16-byte chunk per lane holds 8 bf16 or 4 fp32 columns; a row is 8 (bf16) or 16 (fp32)
+  // chunks, so one wave load covers 8 or 4 rows and a wave's 32 rows take 4 or 8 loads
+  constexpr int kPer = kBf16 ? 8 : 4;            // columns per chunk
+  constexpr int kChunks = kCols / kPer;          // chunks per row
+  constexpr int kRowsPer = 64 / kChunks;         // rows per wave load
+  constexpr int kLoads = 32 / kRowsPer;
+  const int ch = lane % kChunks, rl = lane / kChunks;
+  uint4 v[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = wave * 32 + i * kRowsPer + rl;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
     if (r < rows) {
-      if (kBf16) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(x) +
-                                                              (long)(r0 + r) * ld_x + c0 + 2 * lane);
-        a = __uint_as_float(w << 16);
-        b = __uint_as_float(w & 0xFFFF0000u);
+      const char* src = reinterpret_cast<const char*>(x) +
+                        ((long)(r0 + r) * ld_x + c0 + ch * kPer) * (kBf16 ? 2 : 4);
+      v[i] = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = wave * 32 + i * kRowsPer + rl;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (kBf16) {
+        tile[ch * 8 + 2 * j][r] = __uint_as_float(w[j] << 16);
+        tile[ch * 8 + 2 * j + 1][r] = __uint_as_float(w[j] & 0xFFFF0000u);
       } else {
-        const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(x) + (long)(r0 + r) * ld_x +
-                                                          c0 + 2 * lane);
-        a = v.x;
-        b = v.y;
+        tile[ch * 4 + j][r] = __uint_as_float(w[j]);
       }
     }
-    tile[2 * lane][r] = a;
-    tile[2 * lane + 1][r] = b;
   }
   __syncthreads();
-  const int col = tid >> 1, half = tid & 1;
-  const float* v = &tile[col][half * 64];
+  const int col = tid >> 2, qtr = tid & 3;
+  const float* vv = &tile[col][qtr * 32];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(vv[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
   const float sc = tile_scale(amax, pow2 != 0);
-  uint8_t* dst = qt + (long)(c0 + col) * ld_q + p0 + half * 64;
+  uint8_t* dst = qt + (long)(c0 + col) * ld_q + p0 + qtr * 32;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     uint32_t wd[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float* vv = v + 16 * i + 4 * j;
-      wd[j] = e4m3_encode4(vv[0] / sc, vv[1] / sc, vv[2] / sc, vv[3] / sc);
+      const float* e = vv + 16 * i + 4 * j;
+      wd[j] = e4m3_encode4(e[0] / sc, e[1] / sc, e[2] / sc, e[3] / sc);
     }
     reinterpret_cast<uint4*>(dst)[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
-  if (half == 0) st[(long)(c0 + col) * (ld_q >> 7) + (p0 >> 7)] = sc;
+  if (qtr == 0) st[(long)(c0 + col) * (ld_q >> 7) + (p0 >> 7)] = sc;
 }
 
 // Row-major e4m3 W [G][N][K] -> W^T [G][K][N] in MFMA-fragment order (see pack_kernel): the
@@ -142,14 +158,16 @@ __global__ __launch_bounds__(256) void transpose_scales_kernel(const float* __re
 
 // ---------------------------------------------------------------------------
 // wgrad: out[g][i][j] = sum over group g's padded rows k of A_t[i][k] * B_t[j][k], by 128-wide K
-// blocks with their 128x1 tile scales.  Workgroup: 8 waves (2 x 4), output tile 128 (i) x 256
+// blocks with their 128x1 tile scales.  Workgroup: 4 waves (2 x 2), output tile 128 (i) x 128
 // (j), wave tile 64 x 64.  Both operands are row-major with K contiguous and go global -> LDS by
 // LDS-DMA as whole 128-byte rows (8 rows per wave load), the 16-byte chunk index XORed by
 // row % 8 (bank-conflict-free fragment reads); their per-row scales ride in the same stage.
-// 3 stages, one barrier per K block.
+// 2 stages of 33 KB, one barrier per K block: a group's K is a few blocks at most sizes, and the
+// 66 KB let two workgroups share a CU, so one's loads overlap the other's fp32 stores (the
+// output, not the K loop, is what costs: 64 KB of fp32 per tile against 32 KB of operands per
+// K block).
 namespace {
-constexpr int kWgStages = 3;
-constexpr int kWgA = 128 * 128, kWgB = 256 * 128, kWgS = 384 * 4;   // bytes per stage
+constexpr int kWgA = 128 * 128, kWgB = 128 * 128, kWgS = 256 * 4;   // bytes per stage
 constexpr int kWgStage = kWgA + kWgB + kWgS;
 
 __device__ __forceinline__ void wg_dma16(const void* g, uint8_t* lds) {
@@ -180,51 +198,45 @@ struct WgradArgs {
 };
 
 template <bool SCALED>
-__global__ __launch_bounds__(512) void wgrad_gemm_kernel(const WgradArgs args) {
+__global__ __launch_bounds__(256) void wgrad_gemm_kernel(const WgradArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[kWgStage];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[kWgStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem2[kWgStage];
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;       // 64-row, 64-column wave tile
-  const int ti_n = args.Na >> 7, tj_n = (args.Nb + 255) >> 8;
+  const int ti_n = args.Na >> 7, tj_n = (args.Nb + 127) >> 7;
   const int per_group = ti_n * tj_n;
   const int t = blockIdx.x;
   const int g = t / per_group, rem = t - g * per_group;
   const int ti = rem / tj_n, tj = rem - ti * tj_n;
-  const int i0 = ti * 128, j0 = tj * 256;
+  const int i0 = ti * 128, j0 = tj * 128;
   const int kb0 = args.padded[g] >> 7, nk = (args.padded[g + 1] >> 7) - kb0;
   const int ld = args.ld, lds_ = ld >> 7;
 
-  // per-lane sources: A wave loads cover rows 8 li .. +7 (li = 2 wave + i), B rows 8 li .. (li = 4 wave + i)
-  const uint8_t* a_src[2];
+  // per-lane sources: wave load i covers A rows and B rows 8 li .. +7 (li = 4 wave + i)
+  const uint8_t* a_src[4];
   const uint8_t* b_src[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * (2 * wave + i) + (lane >> 3);
-    a_src[i] = args.a_t + (long)(i0 + r) * ld + 16 * ((lane & 7) ^ (r & 7)) + (long)kb0 * 128;
-  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 8 * (4 * wave + i) + (lane >> 3);
+    a_src[i] = args.a_t + (long)(i0 + r) * ld + 16 * ((lane & 7) ^ (r & 7)) + (long)kb0 * 128;
     const int jr = min(j0 + r, args.Nb - 1);     // rows past Nb (a partial last tile) read the last row, discarded
     b_src[i] = args.b_t + (long)jr * ld + 16 * ((lane & 7) ^ (r & 7)) + (long)kb0 * 128;
   }
-  // one 4-byte scale DMA per wave and K block: waves 0, 1 the A rows 64 w .. +63, waves 2..5 the
-  // B rows 64 (w - 2) .. +63, waves 6, 7 repeat wave 5's (equal load counts per wave)
-  const int sw = wave < 6 ? wave : 5;
+  // one 4-byte scale DMA per wave and K block: waves 0, 1 the A rows 64 w .. +63, waves 2, 3 the
+  // B rows 64 (w - 2) .. +63
   const float* s_src;
-  if (sw < 2) s_src = args.a_ts + (long)(i0 + 64 * sw + lane) * lds_ + kb0;
-  else s_src = args.b_ts + (long)min(j0 + 64 * (sw - 2) + lane, args.Nb - 1) * lds_ + kb0;
-  constexpr int kLoads = 2 + 4 + 1;
+  if (wave < 2) s_src = args.a_ts + (long)(i0 + 64 * wave + lane) * lds_ + kb0;
+  else s_src = args.b_ts + (long)min(j0 + 64 * (wave - 2) + lane, args.Nb - 1) * lds_ + kb0;
 
 #define WG_ISSUE(kb_, dst_)                                                                      \
   {                                                                                              \
     uint8_t* d_ = (dst_);                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i) wg_dma16(a_src[i] + (kb_) * 128, d_ + (2 * wave + i) * 1024); \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                               \
-        wg_dma16(b_src[i] + (kb_) * 128, d_ + kWgA + (4 * wave + i) * 1024);                     \
-    wg_dma4(s_src + (kb_), d_ + kWgA + kWgB + sw * 256);                                         \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+      wg_dma16(a_src[i] + (kb_) * 128, d_ + (4 * wave + i) * 1024);                              \
+      wg_dma16(b_src[i] + (kb_) * 128, d_ + kWgA + (4 * wave + i) * 1024);                       \
+    }                                                                                            \
+    wg_dma4(s_src + (kb_), d_ + kWgA + kWgB + wave * 256);                                       \
   }
 
   v4f acc[4][4];
@@ -270,33 +282,31 @@ __global__ __launch_bounds__(512) void wgrad_gemm_kernel(const WgradArgs args) {
       }
     }
   };
-  // K loop: block kb waits for its own loads (the next may stay in flight), barrier, issue
-  // kb + 2, compute kb; run-time bounds (a group's K is a few blocks at most sizes)
+  // K loop: block kb waits for its own loads (none other is in flight), barrier (every wave's
+  // loads of kb have landed and every wave is done with kb - 1, whose stage kb + 1 now takes),
+  // issue kb + 1, compute kb; run-time bounds (a group's K is a few blocks at most sizes)
   if (nk > 0) {
     WG_ISSUE(0, smem0);
-    WG_ISSUE(nk > 1 ? 1 : 0, smem1);
-    for (int kb = 0; kb < nk; kb += 3) {
+    for (int kb = 0; kb < nk; kb += 2) {
 #define WG_STEP(k_, cur_, nxt_)                                                                  \
   if ((k_) < nk) {                                                                               \
-    if ((k_) + 1 < nk) wg_wait_vmcnt<kLoads>(); else wg_wait_vmcnt<0>();                         \
+    wg_wait_vmcnt<0>();                                                                          \
     wg_barrier();                                                                                \
-    if ((k_) + 2 < nk) WG_ISSUE((k_) + 2, nxt_);                                                 \
+    if ((k_) + 1 < nk) WG_ISSUE((k_) + 1, nxt_);                                                 \
     compute(cur_);                                                                               \
   }
-      WG_STEP(kb, smem0, smem2);
+      WG_STEP(kb, smem0, smem1);
       WG_STEP(kb + 1, smem1, smem0);
-      WG_STEP(kb + 2, smem2, smem1);
 #undef WG_STEP
     }
-    wg_wait_vmcnt<0>();
   }
 #undef WG_ISSUE
-  // epilogue: each wave's 64 x 64 fp32 tile through its own LDS slice (16 KB: three stages hold
-  // 8 of them), read back by rows for 16-byte nontemporal stores; columns XOR-swizzled by row
+  // epilogue: each wave's 64 x 64 fp32 tile through its own LDS slice (16 KB: the two stages
+  // hold the four), read back by rows for 16-byte nontemporal stores; columns XOR-swizzled by row
   // bits 2-3 so the four quads' writes of a fragment row fall on distinct banks
   wg_barrier();                                   // every wave is past its last read of the stages
-  uint8_t* const arr = wave < 3 ? smem0 : (wave < 6 ? smem1 : smem2);
-  float* const wt = reinterpret_cast<float*>(arr + (wave % 3) * 16384);
+  uint8_t* const arr = wave < 2 ? smem0 : smem1;
+  float* const wt = reinterpret_cast<float*>(arr + (wave % 2) * 16384);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -326,7 +336,7 @@ hipError_t launch_quant_128x1_grouped(const void* x, bool bf16, int ld_x, const 
                                       const int32_t* padded, int M_pad_max, int N, uint8_t* qt, int ld_q, float* st,
                                       bool pow2, hipStream_t s) {
   if (M_pad_max == 0 || N == 0) return hipSuccess;
-  const dim3 grid((unsigned)(M_pad_max / 128), (unsigned)(N / 128));
+  const dim3 grid((unsigned)(M_pad_max / 128), (unsigned)(N / 64));
   if (bf16)
     quant_128x1_grouped_kernel<true><<<grid, 256, 0, s>>>(x, ld_x, offsets, G, padded, N, qt, ld_q, st, pow2);
   else
@@ -347,11 +357,11 @@ hipError_t launch_pack_transposed(const uint8_t* src, const float* s, int G, int
 
 hipError_t launch_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_t, const float* b_ts,
                         const int32_t* padded, int G, int Na, int Nb, int ld, float* out, bool pow2, hipStream_t st) {
-  const long tiles = (long)G * (Na / 128) * ((Nb + 255) / 256);
+  const long tiles = (long)G * (Na / 128) * ((Nb + 127) / 128);
   if (tiles == 0) return hipSuccess;
   WgradArgs a{a_t, a_ts, b_t, b_ts, padded, G, Na, Nb, ld, out};
-  if (pow2) wgrad_gemm_kernel<true><<<(unsigned)tiles, 512, 0, st>>>(a);
-  else wgrad_gemm_kernel<false><<<(unsigned)tiles, 512, 0, st>>>(a);
+  if (pow2) wgrad_gemm_kernel<true><<<(unsigned)tiles, 256, 0, st>>>(a);
+  else wgrad_gemm_kernel<false><<<(unsigned)tiles, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

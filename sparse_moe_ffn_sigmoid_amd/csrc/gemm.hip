@@ -24,8 +24,9 @@
 // access (coalesced from HBM, bank-conflict free in LDS).
 //
 // Two kernels:
-//  * stream_gemm_kernel (groups of <= 16 rows, decode): B bypasses LDS and
-//    streams from HBM into registers; the weight bytes are the whole cost.
+//  * stream_gemm_kernel (groups of about 10 rows or fewer on average, decode): B
+//    bypasses LDS and streams from HBM into registers; the weight bytes are the
+//    whole cost.
 //  * mfma_gemm_kernel (larger groups, prefill and dense layers): A and B tiles
 //    go global -> LDS by LDS-DMA through a 3-stage pipeline, one barrier per
 //    K block.
@@ -207,8 +208,8 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& s
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming variant for groups of at most 16 rows (decode-sized
-// batches).  Each B byte is used by exactly one wave, so B bypasses LDS: every
+// Weight-streaming variant for decode-sized batches (16-row tiles; a group of more rows takes
+// one tile per 16 rows, each streaming the group's weights).  Each B byte is used by exactly one wave, so B bypasses LDS: every
 // lane loads its own MFMA fragments straight from HBM (fragment-ordered
 // weights: two 1 KB contiguous wave loads per 16 rows and K block, and a wave's
 // whole stream over K is one contiguous range), with P K blocks of loads in
@@ -1007,10 +1008,10 @@ static void launch_mfma_cfg(const GemmArgs& args, dim3 grid, hipStream_t st) {
   else mfma_gemm_kernel<WM, WN, MT, EPI, false><<<grid, 64 * WM * WN, 0, st>>>(args);
 }
 
-// bm = rows per tile: 32, 64 or 128.  Tiles of 64 or more rows run 8 waves with 64-column
+// bm = rows per tile: 64 or 128.  The plain and SwiGLU epilogues run 8 waves with 64-column
 // wave tiles (two waves per SIMD: one's LDS reads and VALU work overlap the other's MFMAs;
 // measured 5-15% faster for the FP8 down GEMM than 4 waves with 128-column wave tiles, which
-// need half the LDS reads per MFMA); 32-row tiles run 4 waves.
+// need half the LDS reads per MFMA); the scatter epilogue runs 4 waves.
 template <int MT>
 static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
   const bool swiglu = epi == kEpiSwiglu;
@@ -1026,16 +1027,13 @@ static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
   const dim3 grid((unsigned)(8 * per_xcd));
   switch (epi) {
     case kEpiSwiglu:
-      if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiSwiglu>(args, grid, st);
-      else launch_mfma_cfg<2, 2, MT, kEpiSwiglu>(args, grid, st);
+      launch_mfma_cfg<2, 4, MT, kEpiSwiglu>(args, grid, st);
       break;
     case kEpiF32:
-      if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiF32>(args, grid, st);
-      else launch_mfma_cfg<2, 2, MT, kEpiF32>(args, grid, st);
+      launch_mfma_cfg<2, 4, MT, kEpiF32>(args, grid, st);
       break;
     case kEpiBf16:
-      if constexpr (MT >= 2) launch_mfma_cfg<2, 4, MT, kEpiBf16>(args, grid, st);
-      else launch_mfma_cfg<2, 2, MT, kEpiBf16>(args, grid, st);
+      launch_mfma_cfg<2, 4, MT, kEpiBf16>(args, grid, st);
       break;
     default: launch_mfma_cfg<2, 2, MT, kEpiScatter>(args, grid, st); break;
   }
@@ -1045,17 +1043,23 @@ static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
 hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st) {
   switch (bm) {
     case 16: return launch_stream(args, epi, st);
-    case 32: return launch_mfma<1>(args, epi, st);
     case 64: return launch_mfma<2>(args, epi, st);
     default: return launch_mfma<4>(args, epi, st);
   }
 }
 
+// Tile rows from the average group size (the host does not know the groups' sizes).  Measured
+// on the V3 layer from T = 64 to 4096 tokens (per layer, ms): the weight-streaming kernel wins up
+// to 10 rows per expert (T = 320: 1.99 against 2.04 for 64-row tiles) and loses from 11 (T = 352:
+// 2.07 against 2.03; T = 512: 2.74 against 2.10), since its experts with more than 16 rows stream
+// their weights once per 16-row tile; 64-row tiles beat 32-row ones everywhere (T = 1024: 2.28
+// against 3.28 ms) and 128-row ones up to 56 rows per expert (T = 1536: 2.48 against 2.53;
+// T = 2048, 64 rows: 3.0 against 2.75).  A single group (the dense layer) has exactly its rows,
+// so 64-row tiles hold it up to 64.
 int gemm_pick_bm(long rows_upper, int groups) {
   const long avg = groups > 0 ? rows_upper / groups : rows_upper;
-  if (avg <= 16) return 16;
-  if (avg <= 32) return 32;
-  if (avg <= 64) return 64;
+  if (avg <= 10) return 16;
+  if (avg <= (groups > 1 ? 56 : 64)) return 64;
   return 128;
 }
 

@@ -231,11 +231,12 @@ def _gemm_case(seed, M_groups, N, K, gather_rows=None):
     return a_q, a_s, b_q, b_s, offsets, gather
 
 
-# Group sizes pick the kernel: <= 16 rows on average the weight-streaming kernel, else the LDS
-# tile kernel with 32-, 64- or 128-row tiles; a group's partial last tile runs the kernel's
+# Group sizes pick the kernel: <= 10 rows on average the weight-streaming kernel, else the LDS
+# tile kernel with 64- or 128-row tiles; a group's partial last tile runs the kernel's
 # partial-tile path (row blocks past the group's end skipped).
 GEMM_CASES = [
     ([16], 128, 128, None),
+    ([9], 128, 128, None),                           # weight-streaming path, one group
     ([1, 0, 37, 5, 130, 0, 64], 256, 384, None),
     ([300, 2, 0, 77], 512, 256, 120),
     ([2000], 384, 512, None),

@@ -150,7 +150,7 @@ def _ue8m0_case(seed, mg, N, K):
 
 # Power-of-two scales enter the GEMMs without a per-block promotion: as the FP8 MFMA's E8M0 scale
 # operands (down GEMM) or in the exact bf16 conversion (SwiGLU GEMM).  Group sizes pick the
-# weight-streaming kernel (<= 16 rows per group on average) or the LDS tile kernel.
+# weight-streaming kernel (<= 10 rows per group on average) or the LDS tile kernel.
 @pytest.mark.parametrize("mg,W,K", [([7, 0, 130, 64], 256, 512), ([3, 5, 0, 9, 2], 256, 384),
                                     ([161, 120, 150], 2048, 7168)])
 def test_grouped_gemm_swiglu_ue8m0(mg, W, K):
