@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import synth
-from oracle import e4m3, gemm, permute, quant, route
+from oracle import backward, e4m3, gemm, permute, quant, route
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,60 @@ def test_e4m3_encoder_every_midpoint_and_random_fp32():
     q, s = moe.fp8_quant_1x128(to_dev(np.ascontiguousarray(tiles)))
     assert np.all(s.cpu().numpy() == 1.0)
     assert np.array_equal(q.cpu().numpy(), e4m3.encode(tiles))
+
+
+def _near_midpoint_values(amax: np.float32, count: int, seed: int) -> np.ndarray:
+    """fp32 values v whose quotients fp32(v / s), s = fp32(amax / 448), fall on or within a few ulps
+    of e4m3 rounding midpoints (the quantisers take a product with fp32(1 / s) instead of the
+    division away from them; these probe the switch), with both signs."""
+    s = np.float32(amax) / np.float32(448.0)
+    vals, _ = e4m3.finite_positive_grid()
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    mids = mids[mids < 440]
+    t = [mids]
+    lo, hi = mids.copy(), mids.copy()
+    for _ in range(5):
+        lo = np.nextafter(lo, np.float32(0))
+        hi = np.nextafter(hi, np.float32(1000))
+        t += [lo, hi]
+    t = np.concatenate(t)
+    v = (t * s).astype(np.float32)
+    v = v[np.abs(v) < np.float32(amax)]
+    r = np.random.default_rng(seed)
+    v = r.choice(v, count) * r.choice(np.array([-1, 1], np.float32), count)
+    return v.astype(np.float32)
+
+
+@pytest.mark.parametrize("amax", [1.0, 3.7, 0.0031415926, 123.456, 7e-20, 1.3 * 2.0 ** -100, 448.0 * 1.1])
+def test_quantisers_at_quotient_midpoints(amax):
+    """Every quantiser (1x128 and 128x128 from fp32, the transposed 128x1) against the oracle on tiles
+    whose quotients sit at and beside e4m3 rounding midpoints, for scales with many mantissa bits."""
+    say(f"quantisers at quotient midpoints, amax {amax:g}")
+    a = np.float32(amax)
+    v = _near_midpoint_values(a, 256 * 1024, int(amax * 1000) % 97)
+    # 1x128: 2048 rows, element 0 of each row is the amax
+    t1 = v[: 2048 * 127].reshape(2048, 127)
+    x1 = np.concatenate([np.full((2048, 1), a, np.float32), t1], axis=1)
+    q, s = moe.fp8_quant_1x128(to_dev(x1))
+    wq, ws = quant.quant_1x128(x1)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), wq)
+    # 128x128: 2 x 8 blocks, each with the amax at its corner
+    x2 = v[: 256 * 1024].reshape(256, 1024).copy()
+    x2[::128, ::128] = a
+    q, s = moe.fp8_quant_128x128(to_dev(x2))
+    wq, ws = quant.quant_128x128(x2)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), wq)
+    # 128x1 over two groups of 256 and 200 rows: the amax heads each column of each 128-row tile
+    x3 = v[: 456 * 512].reshape(456, 512).copy()
+    x3[[0, 128, 256, 384], :] = a
+    off = np.array([0, 256, 456], np.int32)
+    q, s, po = moe.fp8_quant_128x1_grouped(to_dev(x3), to_dev(off))
+    wq, ws, wpo = backward.quant_128x1_grouped(x3, off)
+    mp = int(wpo[-1])
+    assert np.array_equal(q.cpu().numpy()[:, :mp], wq)
+    assert np.array_equal(s.cpu().numpy()[:, :mp // 128].view(np.uint32), ws.view(np.uint32))
 
 
 @pytest.mark.parametrize("rows,cols", [(128, 128), (384, 256), (4096, 7168)])
