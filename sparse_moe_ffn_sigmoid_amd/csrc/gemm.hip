@@ -697,7 +697,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  ab8[j], e4m3x8_to_bf16_scaled((uint32_t)bf[f][2 * j], (uint32_t)bf[f][2 * j + 1], sbf), acc[mi][f], 0,
+                  e4m3x8_to_bf16_scaled((uint32_t)bf[f][2 * j], (uint32_t)bf[f][2 * j + 1], sbf), ab8[j], acc[mi][f], 0,
                   0, 0);
           }
         } else {
@@ -708,36 +708,49 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
         }
         continue;
       }
-      const float c0[4] = {sa4.x * sb0, sa4.y * sb0, sa4.z * sb0, sa4.w * sb0};
-      const float c1[4] = {sa4.x * sb1, sa4.y * sb1, sa4.z * sb1, sa4.w * sb1};
-      v8bf ab8[4];
       if constexpr (kExact) {
+        // the weights are the MFMA's first operand here, so the lane's 4 outputs of a tile are 4
+        // columns of one row (r0 + r16) and share one scale product per K block: sa x sb_gate and
+        // sa x sb_up for the row, two multiplies per row block instead of eight
+        const float sa_row = *reinterpret_cast<const float*>(st - lane_off + A_BYTES + B_BYTES + (r0 >> 5) * 256 +
+                                                             ((r0 & 31) + r16) * 4);
+        const float cg = sa_row * sb0, cu = sa_row * sb1;
+        v8bf ab8[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) ab8[j] = e4m3x8_to_bf16((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1]);
-      }
 #pragma unroll
-      for (int f0 = 0; f0 < NTW; f0 += 4) {       // promote in groups of 4 tiles: fewer live partials
-        v4f part[4];
+        for (int f0 = 0; f0 < NTW; f0 += 4) {     // promote in groups of 4 tiles: fewer live partials
+          v4f part[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int f = f0 + u;
-          if constexpr (kExact) {
+          for (int u = 0; u < 4; ++u) {
+            const int f = f0 + u;
             v4f t = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  ab8[j], e4m3x8_to_bf16((uint32_t)bf[f][2 * j], (uint32_t)bf[f][2 * j + 1]), t, 0, 0, 0);
+                  e4m3x8_to_bf16((uint32_t)bf[f][2 * j], (uint32_t)bf[f][2 * j + 1]), ab8[j], t, 0, 0, 0);
             part[u] = t;
-          } else {
-            part[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[f], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                                       0, 0, 0);
           }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[mi][f0 + u][i] = fmaf(part[u][i], f0 + u >= NTW / 2 ? cu : cg, acc[mi][f0 + u][i]);
         }
+        continue;
+      }
+      const float c0[4] = {sa4.x * sb0, sa4.y * sb0, sa4.z * sb0, sa4.w * sb0};
+#pragma unroll
+      for (int f0 = 0; f0 < NTW; f0 += 4) {       // promote in groups of 4 tiles: fewer live partials
+        v4f part[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          part[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[f0 + u], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                     0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[mi][f0 + u][i] = fmaf(part[u][i], (kExact && f0 + u >= NTW / 2) ? c1[i] : c0[i], acc[mi][f0 + u][i]);
+          for (int i = 0; i < 4; ++i) acc[mi][f0 + u][i] = fmaf(part[u][i], c0[i], acc[mi][f0 + u][i]);
       }
     }
   };
@@ -886,8 +899,9 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
   const int ld_out = si ? s1.ld_out : s0.ld_out;
   const int32_t* const dst_row = si ? s1.dst_row : s0.dst_row;
   const float* const row_w = si ? s1.row_w : s0.row_w;
-  // lane holds rows wm*16*MT + 16 mi + 4q + i of the tile; plain: columns nt*256 + wn*16*NTW + 16 f + r16;
-  // SwiGLU: h columns nt*128 + wn*8*NTW + 16 j + r16 (gate f = j, up f = NTW/2 + j)
+  // plain: lane holds rows wm*16*MT + 16 mi + 4q + i of the tile, columns nt*256 + wn*16*NTW + 16 f + r16;
+  // SwiGLU (weights as the MFMA's first operand): lane holds row wm*16*MT + 16 mi + r16, h columns
+  // nt*128 + wn*8*NTW + 16 j + 4q + i (gate f = j, up f = NTW/2 + j)
   if constexpr (EPI == kEpiSwiglu) {
     constexpr int H = NTW / 2;
     float h[MT][H][4];
@@ -898,15 +912,16 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
 #pragma unroll
         for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][H + j][i]);
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
+    for (int mi = 0; mi < MT; ++mi) {
+      float mx = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = 0.0f;
+      for (int j = 0; j < H; ++j)
 #pragma unroll
-        for (int j = 0; j < H; ++j) mx = fmaxf(mx, fabsf(h[mi][j][i]));
-        mx = group_max<16>(mx);
-        if (r16 == 0) red[wn][wm * 16 * MT + mi * 16 + 4 * q + i] = mx;
-      }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(h[mi][j][i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));             // the row's four quads
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (q == 0) red[wn][wm * 16 * MT + mi * 16 + r16] = mx;
+    }
     __syncthreads();                                // also: every wave is past its last LDS stage read
     // one thread per row: the tile's amax, its scale and the scale's reciprocal (red[0][r] and
     // red[1][r] then hold sc and 1/sc; only this thread reads row r's partial maxima)
@@ -923,18 +938,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_gemm_kernel(const GemmArgs 
     lds_barrier();
     uint8_t* stage = smem0;                         // BM x 128 codes
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
+    for (int mi = 0; mi < MT; ++mi) {
+      const int r = wm * 16 * MT + mi * 16 + r16;
+      const float inv = red[1][r];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 16 * MT + mi * 16 + 4 * q + i;
-        const float inv = red[1][r];
-#pragma unroll
-        for (int j = 0; j < H; j += 2) {
-          const uint32_t c2 = e4m3_encode2(h[mi][j][i] * inv, h[mi][j + 1][i] * inv);
-          stage[r * 128 + wn * 16 * H + 16 * j + r16] = (uint8_t)c2;
-          stage[r * 128 + wn * 16 * H + 16 * (j + 1) + r16] = (uint8_t)(c2 >> 8);
-        }
-      }
+      for (int j = 0; j < H; ++j)
+        *reinterpret_cast<uint32_t*>(stage + r * 128 + wn * 16 * H + 16 * j + 4 * q) =
+            e4m3_encode4(h[mi][j][0] * inv, h[mi][j][1] * inv, h[mi][j][2] * inv, h[mi][j][3] * inv);
+    }
     __syncthreads();
     for (int ci = tid; ci < BM * 8; ci += 64 * NW) {
       const int r = ci >> 3, c = ci & 7;
