@@ -310,8 +310,8 @@ def _sizes(seed, G, lo, hi):
 # More than 64 groups: each lane of the tile lookup then scans several groups (G = 65 leaves the
 # second lane one group), up to the largest G the call takes.
 GEMM_CASES += [
-    (_sizes(1, 200, 0, 20), 256, 256, 300),          # weight-streaming kernel, 4 groups per lane
-    (_sizes(2, 70, 0, 50), 384, 256, None),          # 32-row tiles
+    (_sizes(1, 200, 0, 20), 256, 256, 300),          # weight-streaming kernel (10 rows per group), 4 groups per lane
+    (_sizes(2, 70, 0, 50), 384, 256, None),          # 64-row tiles, 27 rows per group on average
     (_sizes(3, 130, 10, 90), 256, 384, None),        # 64-row tiles
     (_sizes(4, 65, 60, 200), 256, 256, 500),         # 128-row tiles, partial second tiles
     (_sizes(5, 1024, 0, 6), 128, 128, None),         # G = 1024: 16 groups per lane
