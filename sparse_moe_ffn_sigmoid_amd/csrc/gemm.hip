@@ -238,13 +238,35 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
   // every lane whatever EXEC holds, so those branches must be scalar
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, r16 = lane & 15,
             q = lane >> 4;
+  // (m tile, n tile) of this workgroup.  NFAST: the grid's x is the n tile.  Otherwise the grid is
+  // (m tiles, n tiles), and when the static segment (the shared expert) has 2..8 m tiles and the
+  // n tiles come in multiples of 8, the first ms x ny workgroups in dispatch order take its tiles
+  // so that the m tiles of one n tile are 8 workgroups apart: the same XCD (workgroups go to the
+  // 8 XCDs round-robin), whose L2 then serves their shared weight stream; the other workgroups
+  // take the dynamic segment's tiles in the grid's own order (m tile fastest).
+  int tm = NFAST ? blockIdx.y : blockIdx.x, tn = NFAST ? blockIdx.x : blockIdx.y;
+  if constexpr (!NFAST) {
+    const int ms = args.seg[0].m_tiles, ny = gridDim.y, mt = gridDim.x;
+    if (ms >= 2 && ms <= 8 && ny % 8 == 0 && mt > ms) {
+      const int L = blockIdx.y * mt + blockIdx.x;   // dispatch order
+      if (L < ms * ny) {
+        const int b = L / (8 * ms), rem = L - b * 8 * ms;
+        tm = rem >> 3;
+        tn = 8 * b + (rem & 7);
+      } else {
+        const int L2 = L - ms * ny, md = mt - ms;
+        tm = ms + L2 % md;
+        tn = L2 / md;
+      }
+    }
+  }
   int si, g, m0, m_end;
-  if (!find_tile(args, 16, NFAST ? blockIdx.y : blockIdx.x, si, g, m0, m_end)) return;
+  if (!find_tile(args, 16, tm, si, g, m0, m_end)) return;
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& s1 = args.seg[1];
   const int K = si ? s1.K : s0.K, nkb = K >> 7;
   const int half = (si ? s1.N : s0.N) / NB;
-  const int nbase = (NFAST ? blockIdx.x : blockIdx.y) * 4 * CW;   // first column of this workgroup in each block
+  const int nbase = tn * 4 * CW;                 // first column of this workgroup in each block
   if (nbase >= half) return;
   const int ncol0 = nbase + wave * CW;         // first column of this wave in each block
   const bool wave_live = ncol0 < half;          // all waves live when half % (4 CW) == 0
