@@ -101,6 +101,42 @@ __global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* 
   }
 }
 
+// Wave-wide maximum of a 64-bit key, every lane receiving it: DPP exchanges within each row of 16
+// lanes (pairs, quads, half rows mirrored, rows mirrored), then the four rows' maxima read as
+// scalars.  DPP moves are VALU operations; the LDS-routed lane shuffles they replace wait on the
+// LDS pipe at every step of the argmax rounds below.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o = dpp_u64<0xB1>(v);                  // quad_perm [1, 0, 3, 2]
+  v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v);                           // quad_perm [2, 3, 0, 1]
+  v = o > v ? o : v;
+  o = dpp_u64<0x141>(v);                          // row_half_mirror
+  v = o > v ? o : v;
+  o = dpp_u64<0x140>(v);                          // row_mirror
+  v = o > v ? o : v;
+  uint64_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * i) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * i);
+  const uint64_t a = r[0] > r[1] ? r[0] : r[1], b = r[2] > r[3] ? r[2] : r[3];
+  return a > b ? a : b;
+}
+
+// Order-preserving key of a biased score and its expert: a larger score wins, equal scores (-0 and
+// +0 equal) go to the lower expert id; 0 is below every key.
+__device__ __forceinline__ uint64_t route_key(float b, int e) {
+  const uint32_t f = __float_as_uint(b + 0.0f);   // -0 -> +0
+  const uint32_t u = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0x7FFFFFFF - e);
+}
+
 // Register-resident routing for the common layouts: lane l holds experts
 // l*EPL .. l*EPL+EPL-1 (EPL = E/64, or 1 when E <= 64), a group is LPG
 // consecutive lanes.  Group top-2 merges pairs across the group's lanes with
@@ -143,40 +179,33 @@ __global__ __launch_bounds__(256) void route_reg_kernel(const float* __restrict_
   const float gscore = (rule == 1 || gsz == 1) ? t1 : t1 + t2;
   const int mygroup = lane / lpg;
   int rank = 0;
-  for (int g = 0; g < G; ++g) {
-    const float o = __shfl(gscore, g * lpg);
+  for (int g = 0; g < G; ++g) {                     // g * lpg is the same in every lane: a scalar read
+    const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gscore), g * lpg));
     rank += (o > gscore || (o == gscore && g < mygroup)) ? 1 : 0;
   }
   const bool kept = live && rank < gk;
-  // each round's winner carries its unbiased score along, so the weights need no second
-  // read of the scores
+  // each round's winner carries its unbiased score along (read from the lane that holds it), so
+  // the weights need no second read of the scores
   unsigned taken = 0;
   int mine = 0;
   float mine_s = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float best = -INFINITY, best_s = 0.0f;
-    int bi = INT_MAX;
+    uint64_t key = 0;
+    float key_s = 0.0f;
     if (kept) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        if (!((taken >> i) & 1u) && (b[i] > best || bi == INT_MAX)) {
-          best = b[i];
-          best_s = sv[i];
-          bi = e0 + i;
+        const uint64_t c = route_key(b[i], e0 + i);
+        if (!((taken >> i) & 1u) && c > key) {
+          key = c;
+          key_s = sv[i];
         }
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o), os = __shfl_xor(best_s, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > best || (ov == best && oi < bi)) {
-        best = ov;
-        best_s = os;
-        bi = oi;
-      }
-    }
-    if (bi == INT_MAX) bi = 0;                      // only with NaN scores, outside the contract
+    const uint64_t best = wave_max_u64(key);
+    // no candidate left: only with NaN scores, outside the contract
+    const int bi = best ? 0x7FFFFFFF - (int)(uint32_t)best : 0;
+    const float best_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key_s), bi / EPL));
     if (bi >= e0 && bi < e0 + EPL) taken |= 1u << (bi - e0);
     if (lane == j) {
       mine = bi;
@@ -184,7 +213,7 @@ __global__ __launch_bounds__(256) void route_reg_kernel(const float* __restrict_
     }
   }
   float sum = 0.0f;
-  for (int j = 0; j < k; ++j) sum += __shfl(mine_s, j);
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine_s), j));
   if (lane < k) {
     topk_idx[(long)t * k + lane] = mine;
     topk_w[(long)t * k + lane] = (mine_s / sum) * routed_scale;

@@ -163,6 +163,23 @@ def test_route_given_scores_bit_exact(case):
     assert np.array_equal(w.cpu().numpy().view(np.uint32), want_w.view(np.uint32))
 
 
+@pytest.mark.parametrize("G,gk", [(1, 1), (4, 2)])
+def test_route_signed_zero_ties(G, gk):
+    """Biased scores of +0 (0.5 - 0.5) and -0 (-0 + -0) are equal: ties go to the lower expert id
+    (a kernel ordering +0 above -0 would take the even experts instead)."""
+    say(f"moe_route signed-zero ties G={G} gk={gk}")
+    T, E, k = 8, 16, 4
+    sc = np.where(np.arange(E) % 2 == 0, np.float32(0.5), np.float32(-0.0)).astype(np.float32)
+    sc = np.tile(sc, (T, 1))
+    bias = np.where(np.arange(E) % 2 == 0, np.float32(-0.5), np.float32(-0.0)).astype(np.float32)
+    cfg = moe.MoeConfig(128, 128, E, k, 0, 0, G, gk, 0, 1.0)
+    _, idx, w = moe.moe_route(cfg, T, DEV, scores=to_dev(sc), bias=to_dev(bias))
+    want_idx, want_w = route.select(sc, bias, G, gk, k, 1.0, "top2_sum")
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), want_w.view(np.uint32))
+    assert np.array_equal(np.sort(want_idx[0]), np.arange(k))
+
+
 @pytest.mark.parametrize("shape", [synth.TINY, synth.V3_DECODE, synth.with_tokens(synth.V3_PREFILL, 1000)])
 def test_router_scores(shape):
     say(f"router scores {shape.name} T={shape.tokens}")
