@@ -252,3 +252,35 @@ def test_validation_runs_before_the_launches():
             assert msg.startswith("MOEFP8_VALIDATE check"), (name, msg)
         else:
             assert not msg.startswith("MOEFP8_VALIDATE"), (name, msg)
+
+
+def test_header_compiles_as_c99_and_links_against_the_library(tmp_path):
+    """The boundary is a C ABI: the header compiles as strict C99, and a C program that calls
+    the host-only entry points links against the library and runs (no GPU call is made)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "moefp8.h"\n'
+        "int main(void) {\n"
+        "  moe_cfg_t c = {7168, 2048, 256, 8, 1, 2048, 8, 4, MOE_GROUP_SCORE_TOP2_SUM, 1.0f, MOE_SCALE_F32, 1e-6f};\n"
+        "  size_t ws = moe_ffn_workspace_size(64, &c);\n"
+        "  size_t pr = moe_padded_rows(1000, 8);\n"
+        '  printf("%zu %zu %s\\n", ws, pr, moe_status_string(MOE_ERR_INVALID_DATA));\n'
+        "  return ws > 0 && pr == (size_t)((1000 + 127) / 128 + 8) * 128 ? 0 : 1;\n"
+        "}\n")
+    exe = tmp_path / "abi"
+    lib_path = os.path.join(ROOT, "sparse_moe_ffn_sigmoid_amd", "libmoefp8.so")   # the plain in-tree build
+    if not os.path.exists(lib_path):
+        pytest.skip("the in-tree library is not built")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{os.path.join(ROOT, 'include')}",
+                        str(src), lib_path, f"-Wl,-rpath,{os.path.dirname(lib_path)}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, (r.stdout, r.stderr)
+    assert r.stdout.split()[2] == "MOE_ERR_INVALID_DATA"
