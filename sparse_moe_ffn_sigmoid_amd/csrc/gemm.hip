@@ -225,8 +225,11 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& s
 // for the gate/up GEMM at decode (T = 64): 6.372 GB fetched per launch instead of 6.438 GB for
 // 6.343 GB of algorithmic bytes, 0.924 instead of 0.935 ms.  The down GEMM ran 2.5% slower in
 // that order, and keeps the grid (m tiles, n tiles).
+// Launch bounds: the FP8 kernels with power-of-two scales (NB = 1, SCALED) ask for 3 waves per SIMD;
+// left alone the compiler gave them 208 registers (2 waves), and the down GEMM at decode ran 0.498
+// instead of 0.486 ms.
 template <int NB, int NTW, int P, int EPI, bool SCALED, bool NFAST>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(const GemmArgs args) {
+__global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_kernel(const GemmArgs args) {
   constexpr int NF = NB * NTW;                 // B fragments per lane per K block
   constexpr int CW = 16 * NTW;                 // columns per wave in each B block
   static_assert(EPI != kEpiSwiglu || NTW % 2 == 0, "the SwiGLU epilogue encodes h in pairs");
