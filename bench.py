@@ -18,7 +18,10 @@ from the same steps run again with every stage event; ``cpu_baseline`` times the
 sample of the same workload.  ``roofline.traffic`` is the HBM traffic per launch
 of that kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, stored in
 profiles/<workload>_gate_up_traffic.md together with a hash of the GEMM sources;
-it is reported only while the sources still match (else null).
+it is reported only while the sources still match (else null).  With the default (decode)
+workload the line also carries sub-records timed the same way: ``v3_prefill`` (T = 4096),
+``dense_ffn``, ``v3_skew`` (T = 16384, load-skewed), ``v3_prefill_ue8m0`` (power-of-two scales)
+and ``v3_prefill_backward`` (the routed experts' FP8 dgrad and wgrad).
 
 Helpers for the counter runs:
   --calibrate-copy MIB     a plain copy of MIB MiB (the library's row gather with the identity
@@ -745,6 +748,14 @@ def main():
         sub, _ = time_workload(synth.V3_PREFILL, max(5, args.steps // 2), max(2, args.warmup), ue8m0=args.ue8m0,
                                rmsnorm=args.rmsnorm, deterministic=args.deterministic, with_next_rows=False)
         res["v3_prefill"] = sub
+        # the other MFMA-heavy configurations, timed the same way: the dense FFN layer, the
+        # load-skewed prefill batch, and the V3 prefill with power-of-two (UE8M0) scales
+        for key, sh, ue in (("dense_ffn", synth.DENSE_FFN, args.ue8m0), ("v3_skew", synth.V3_SKEW, args.ue8m0),
+                            ("v3_prefill_ue8m0", synth.V3_PREFILL, True)):
+            if key == "v3_prefill_ue8m0" and args.ue8m0:
+                continue
+            res[key], _ = time_workload(sh, max(5, args.steps // 2), max(2, args.warmup), ue8m0=ue,
+                                        rmsnorm=args.rmsnorm, deterministic=args.deterministic, with_next_rows=False)
         res["v3_prefill_backward"] = time_backward(synth.V3_PREFILL, max(3, args.steps // 10), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
