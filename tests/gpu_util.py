@@ -381,3 +381,50 @@ def compare_router_run(layer, xb, got, tokens=None, chunks=1):
         back = np.argsort(np.argsort(ref["topk_idx"], 1), 1)
         sub["topk_w"] = np.take_along_axis(np.take_along_axis(got["topk_w"][tok], order, 1), back, 1)
     assert_within_error_bound(layer, xv[tok], sub, ref, rows=same, chunks=max(chunks, 4))
+
+
+# ---- sampled tokens at V3 size ----
+
+def tile_edges(offsets, bm=128):
+    """Sorted positions of the first and the last row of the m tiles of every group (of its first
+    two and last two tiles when it has more): a group of n rows has ceil(n / bm) tiles over which
+    its rows are split evenly in whole 16-row blocks (the tile kernel's split), keyed by the
+    group's tile row counts (its tile shape)."""
+    shapes = {}
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        c = -(-n // bm)
+        rb = ((-(-n // c)) + 15) // 16 * 16 if c > 1 else bm
+        edges, rows = [], []
+        for j in range(c):
+            a, b = lo + j * rb, min(lo + (j + 1) * rb, hi)
+            if j < 2 or j >= c - 2:
+                edges += [a, b - 1]
+            rows.append(b - a)
+        shapes.setdefault(tuple(rows), []).append(edges)
+    return shapes
+
+
+def pick_tokens(idx, E, n_min, seed, max_shapes=24):
+    """Tokens whose assignments sit at the first and last rows of the m tiles of one group per tile
+    shape (up to max_shapes shapes, spread over the smallest to the largest), topped up with random
+    tokens to at least n_min."""
+    T, k = idx.shape
+    off, sa, _ = permute.permute(idx, E)
+    shapes = tile_edges(off)
+    keys = sorted(shapes, key=lambda t: (len(t), t))
+    if len(keys) > max_shapes:
+        keys = [keys[i] for i in np.linspace(0, len(keys) - 1, max_shapes).round().astype(int)]
+    toks = set()
+    for key in keys:
+        for p in shapes[key][0]:
+            toks.add(int(sa[p]) // k)
+    r = np.random.default_rng(seed)
+    while len(toks) < n_min:
+        toks.add(int(r.integers(T)))
+    say(f"  {len(toks)} tokens: tile edges of {len(keys)} of {len(shapes)} tile shapes "
+        f"(e.g. {keys[0]}, {keys[len(keys) // 2]}, {keys[-1]}) + random")
+    return sorted(toks)

@@ -14,13 +14,12 @@ import pytest
 import torch
 
 import synth
-from oracle import permute, route
 
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import sparse_moe_ffn_sigmoid_amd as moe
-    from gpu_util import DEV, Layer, assert_output, assert_within_error_bound, bf16_np, say, to_dev
+    from gpu_util import DEV, Layer, assert_output, assert_within_error_bound, bf16_np, pick_tokens, say, to_dev
     from gpu_util import compare_router_run as _compare_router_run
     from gpu_util import run_layer as _run
 
@@ -150,51 +149,6 @@ def v3():
     return Layer(synth.V3_PREFILL)
 
 
-def _tile_edges(offsets, bm=128):
-    """Sorted positions of the first and the last row of the m tiles of every group (of its first
-    two and last two tiles when it has more): a group of n rows has ceil(n / bm) tiles over which
-    its rows are split evenly in whole 16-row blocks (the tile kernel's split), keyed by the
-    group's tile row counts (its tile shape)."""
-    shapes = {}
-    for e in range(len(offsets) - 1):
-        lo, hi = int(offsets[e]), int(offsets[e + 1])
-        n = hi - lo
-        if n == 0:
-            continue
-        c = -(-n // bm)
-        rb = ((-(-n // c)) + 15) // 16 * 16 if c > 1 else bm
-        edges, rows = [], []
-        for j in range(c):
-            a, b = lo + j * rb, min(lo + (j + 1) * rb, hi)
-            if j < 2 or j >= c - 2:
-                edges += [a, b - 1]
-            rows.append(b - a)
-        shapes.setdefault(tuple(rows), []).append(edges)
-    return shapes
-
-
-def _pick_tokens(idx, E, n_min, seed, max_shapes=24):
-    """Tokens whose assignments sit at the first and last rows of the m tiles of one group per tile
-    shape (up to max_shapes shapes, spread over the smallest to the largest), topped up with random
-    tokens to at least n_min."""
-    T, k = idx.shape
-    off, sa, _ = permute.permute(idx, E)
-    shapes = _tile_edges(off)
-    keys = sorted(shapes, key=lambda t: (len(t), t))
-    if len(keys) > max_shapes:
-        keys = [keys[i] for i in np.linspace(0, len(keys) - 1, max_shapes).round().astype(int)]
-    toks = set()
-    for key in keys:
-        for p in shapes[key][0]:
-            toks.add(int(sa[p]) // k)
-    r = np.random.default_rng(seed)
-    while len(toks) < n_min:
-        toks.add(int(r.integers(T)))
-    say(f"  {len(toks)} tokens: tile edges of {len(keys)} of {len(shapes)} tile shapes "
-        f"(e.g. {keys[0]}, {keys[len(keys) // 2]}, {keys[-1]}) + random")
-    return sorted(toks)
-
-
 def _v3_run(v3, shape):
     bias = synth.skew_bias() if shape.skewed else None
     v3.bias = bias
@@ -220,7 +174,7 @@ def test_v3_decode_every_token(v3):
 def test_v3_prefill_sampled_tokens(v3, shape):
     say(f"forward {shape.name} T={shape.tokens} (sampled oracle check)")
     xb, got = _v3_run(v3, shape)
-    toks = _pick_tokens(got["topk_idx"], 256, 32, shape.cfg_id)
+    toks = pick_tokens(got["topk_idx"], 256, 32, shape.cfg_id)
     _compare_router_run(v3, xb, got, tokens=toks, chunks=8)
     v3.bias = None
     v3.weights.bias = None
@@ -248,4 +202,4 @@ def test_ep_local_sampled_tokens():
     got = _run(layer, xb)
     counts = np.bincount(got["topk_idx"].reshape(-1), minlength=s.n_experts)
     say(f"  rows per expert: min {counts.min()}, max {counts.max()}")
-    _compare_router_run(layer, xb, got, tokens=_pick_tokens(got["topk_idx"], s.n_experts, 32, s.cfg_id), chunks=8)
+    _compare_router_run(layer, xb, got, tokens=pick_tokens(got["topk_idx"], s.n_experts, 32, s.cfg_id), chunks=8)

@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import sparse_moe_ffn_sigmoid_amd as moe
-    from gpu_util import DEV, FP8_MFMA_REL, Layer, check_requant, compare_router_run, run_layer, say, to_dev
+    from gpu_util import (DEV, FP8_MFMA_REL, Layer, check_requant, compare_router_run, pick_tokens, run_layer, say,
+                          to_dev)
 
 
 def _gamma_bits(d, seed):
@@ -203,6 +204,21 @@ def test_layer_with_norm_and_ue8m0(shape, ue8m0, with_norm):
     layer = Layer(shape, ue8m0=ue8m0, norm_gamma=_gamma_bits(shape.hidden, 5) if with_norm else None)
     xb = synth.gen_x(shape)
     compare_router_run(layer, xb, run_layer(layer, xb))
+
+
+@pytest.mark.timeout(400)
+def test_layer_v3_prefill_ue8m0_sampled():
+    """The V3 prefill step (T = 4096) with power-of-two scales, as the benchmark times it: tokens at
+    the first and last rows of the m tiles of one expert per tile shape (8 shapes, from a single
+    tile to two split tiles), against the oracle with UE8M0 scales.  Few tokens: the oracle
+    quantises every expert they touch again, with power-of-two scales."""
+    s = synth.V3_PREFILL
+    say("forward V3 prefill with UE8M0 scales, sampled tokens")
+    layer = Layer(s, ue8m0=True)
+    xb = synth.gen_x(s)
+    got = run_layer(layer, xb)
+    toks = pick_tokens(got["topk_idx"], s.n_experts, 16, s.cfg_id, max_shapes=8)
+    compare_router_run(layer, xb, got, tokens=toks, chunks=8)
 
 
 def test_layer_v3_decode_norm_ue8m0_sampled():
