@@ -20,7 +20,11 @@
  *     moe_last_error() gives a message (thread-local, valid until the next call
  *     on the same thread).
  *   - Every array argument is a DEVICE pointer, allocated and owned by the
- *     caller; the library allocates nothing and keeps no state between calls.
+ *     caller; the library allocates nothing and keeps no state between calls
+ *     (moe_ffn_forward_noalloc aside: its workspace is a static device array).
+ *   - Calls enqueue kernels only (no allocation, memset, copy or synchronisation
+ *     unless MOEFP8_VALIDATE is on), so they can be captured into a HIP graph; the
+ *     forward's capture and replay are tested.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work and return; nothing synchronises the host.
  *   - Shapes and pointers are checked on the host before anything is enqueued;
