@@ -18,7 +18,12 @@ namespace moefp8 {
 // 64 x 64 tile, so each token row is read once per 64 experts and each router
 // weight row once per 64 tokens, with 8 waves (two per SIMD: 11 us faster than
 // 4 at 4096 tokens, the loads being latency-bound).
-template <int NW, int NT, int MTK, int U>
+// PARTIAL: the hidden dimension is also split over gridDim.z workgroups (block z
+// takes the z-th of gridDim.z near-equal ranges of K steps), each writing its raw
+// partial logits to out[z][T][E]; router_finish_kernel adds them in order of z and
+// applies the sigmoid.  Small batches use it, so that the router's loads are spread
+// over every CU.
+template <int NW, int NT, int MTK, int U, bool PARTIAL>
 __global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* __restrict__ x,
                                                                 const uint16_t* __restrict__ w, int T, int E, int D,
                                                                 float* __restrict__ scores) {
@@ -28,8 +33,11 @@ __global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r16 = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * 16 * MTK, e0 = blockIdx.y * 16 * NT;
-  const int steps = D >> 5;                     // 32-wide K steps, split as evenly as possible
-  const int s0 = (steps * wave) / NW, s1 = (steps * (wave + 1)) / NW;
+  // 32-wide K steps: this workgroup's range (all of them unless PARTIAL), split as evenly as
+  // possible over its waves
+  const int z = PARTIAL ? (int)blockIdx.z : 0, nz = PARTIAL ? (int)gridDim.z : 1;
+  const int all = D >> 5, kz0 = (all * z) / nz, steps = (all * (z + 1)) / nz - kz0;
+  const int s0 = kz0 + (steps * wave) / NW, s1 = kz0 + (steps * (wave + 1)) / NW;
   const uint16_t* xa[MTK];
 #pragma unroll
   for (int i = 0; i < MTK; ++i) xa[i] = x + (long)min(t0 + 16 * i + r16, T - 1) * D + 8 * q;
@@ -96,7 +104,10 @@ __global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tt = t0 + 16 * i + 4 * q + r;
-      if (tt < T) scores[(long)tt * E + e0 + 16 * j + r16] = 1.0f / (1.0f + expf(-t[r]));
+      if (tt < T) {
+        if constexpr (PARTIAL) scores[((long)z * T + tt) * E + e0 + 16 * j + r16] = t[r];
+        else scores[(long)tt * E + e0 + 16 * j + r16] = 1.0f / (1.0f + expf(-t[r]));
+      }
     }
   }
 }
@@ -291,16 +302,44 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
   }
 }
 
-hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, hipStream_t st) {
+// scores = sigmoid(part[0] + part[1] + ... + part[nz-1]), added in that order; n = T * E (a
+// multiple of 4), one float4 per thread.
+__global__ __launch_bounds__(256) void router_finish_kernel(const float* __restrict__ part, int nz, long n,
+                                                            float* __restrict__ scores) {
+  const long i = blockIdx.x * 256L + threadIdx.x;
+  if (4 * i >= n) return;
+  v4f a = reinterpret_cast<const v4f*>(part)[i];
+  for (int z = 1; z < nz; ++z) a += reinterpret_cast<const v4f*>(part + z * n)[i];
+  v4f o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = 1.0f / (1.0f + expf(-a[r]));
+  reinterpret_cast<v4f*>(scores)[i] = o;
+}
+
+// Batches of up to 512 tokens: 16 x 16 tiles of 16 waves; with a partial-logit buffer of
+// kRouterSplit * T * E floats (the forward lends one) and a hidden dimension of at least 4096,
+// also split 4 ways over the hidden dimension (at T = 64: 256 workgroups instead of 64).
+constexpr int kRouterSplit = 4;
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, float* part,
+                         hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (T <= 512)
-    router_splitk_kernel<16, 1, 1, 8><<<dim3((T + 15) / 16, E / 16), 1024, 0, st>>>(x, w, T, E, D, scores);
-  else if (E % 64 == 0)
-    router_splitk_kernel<8, 4, 4, 2><<<dim3((T + 63) / 64, E / 64), 512, 0, st>>>(x, w, T, E, D, scores);
-  else
-    router_splitk_kernel<4, 1, 4, 4><<<dim3((T + 63) / 64, E / 16), 256, 0, st>>>(x, w, T, E, D, scores);
+  if (T <= 512 && part && D >= 4096) {
+    router_splitk_kernel<16, 1, 1, 8, true><<<dim3((T + 15) / 16, E / 16, kRouterSplit), 1024, 0, st>>>(x, w, T, E, D,
+                                                                                                         part);
+    const long n = (long)T * E;
+    router_finish_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(part, kRouterSplit, n, scores);
+  } else if (T <= 512) {
+    router_splitk_kernel<16, 1, 1, 8, false><<<dim3((T + 15) / 16, E / 16), 1024, 0, st>>>(x, w, T, E, D, scores);
+  } else if (E % 64 == 0) {
+    router_splitk_kernel<8, 4, 4, 2, false><<<dim3((T + 63) / 64, E / 64), 512, 0, st>>>(x, w, T, E, D, scores);
+  } else {
+    router_splitk_kernel<4, 1, 4, 4, false><<<dim3((T + 63) / 64, E / 16), 256, 0, st>>>(x, w, T, E, D, scores);
+  }
   return hipGetLastError();
 }
+
+size_t router_partial_floats(int T, int E) { return (size_t)kRouterSplit * (size_t)T * (size_t)E; }
 
 hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,
                         float routed_scale, int32_t* topk_idx, float* topk_w, hipStream_t st) {

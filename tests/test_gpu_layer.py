@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import synth
+from oracle import route
 
 pytestmark = pytest.mark.gpu
 
@@ -139,6 +140,26 @@ def test_single_token_and_empty_batch(tiny):
     out = moe.moe_ffn_forward(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV), tiny.cfg, tiny.weights,
                               workspace=torch.empty(256, dtype=torch.uint8, device=DEV))
     assert out.shape == (0, 256)
+
+
+ROUTER_SPLIT = synth.MoeShape("router_split", 21, 512, 4096, 128, 16, 4, 1, 128, 4, 2)
+
+
+@pytest.mark.parametrize("T", [1, 64, 512])
+def test_forward_router_scores_split_over_k(T):
+    """Batches of up to 512 tokens with a hidden dimension of 4096 or more: the forward's router
+    splits the hidden dimension over four workgroups and adds their partial logits in a fixed
+    order.  Its scores against the oracle's (the bound of the single-pass router), and the same
+    routing as the oracle's except at near-ties."""
+    s = dataclasses.replace(ROUTER_SPLIT, tokens=T)
+    say(f"forward router with the hidden dimension split: T={T}, hidden {s.hidden}")
+    layer = Layer(s)
+    xb = synth.gen_x(s)
+    got = _run(layer, xb)
+    want = route.sigmoid_scores(route.router_logits(synth.bf16_bits_to_f32(xb),
+                                                    synth.bf16_bits_to_f32(synth.gen_router_w(s))))
+    assert np.abs(got["scores"] - want).max() <= 2e-5
+    _compare_router_run(layer, xb, got)
 
 
 # ---- V3 shapes, in the benchmark's launch configuration, on sampled tokens ----
