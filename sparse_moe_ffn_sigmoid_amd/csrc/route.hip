@@ -316,9 +316,11 @@ __global__ __launch_bounds__(256) void router_finish_kernel(const float* __restr
   reinterpret_cast<v4f*>(scores)[i] = o;
 }
 
-// Batches of up to 512 tokens: 16 x 16 tiles of 16 waves; with a partial-logit buffer of
-// kRouterSplit * T * E floats (the forward lends one) and a hidden dimension of at least 4096,
-// also split 4 ways over the hidden dimension (at T = 64: 256 workgroups instead of 64).
+// Batches of up to 1024 tokens: 16 x 16 tiles of 16 waves (at T = 640 the route + permutation
+// stage took 68 against 80 us with the 64 x 64 tiles, equal at 1024, 80 against 109 us at 1536
+// for the 64 x 64 tiles); up to 512 tokens, with a partial-logit buffer of kRouterSplit * T * E
+// floats (the forward lends one) and a hidden dimension of at least 4096, also split 4 ways over
+// the hidden dimension (at T = 64: 256 workgroups instead of 64).
 constexpr int kRouterSplit = 4;
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, float* part,
@@ -329,7 +331,7 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int
                                                                                                          part);
     const long n = (long)T * E;
     router_finish_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(part, kRouterSplit, n, scores);
-  } else if (T <= 512) {
+  } else if (T <= 1024) {
     router_splitk_kernel<16, 1, 1, 8, false><<<dim3((T + 15) / 16, E / 16), 1024, 0, st>>>(x, w, T, E, D, scores);
   } else if (E % 64 == 0) {
     router_splitk_kernel<8, 4, 4, 2, false><<<dim3((T + 63) / 64, E / 64), 512, 0, st>>>(x, w, T, E, D, scores);
