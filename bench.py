@@ -140,14 +140,17 @@ def gemm_source_hash() -> str:
 
 def gate_up_kernel(shape, ue8m0: bool = False) -> str:
     """Name of the kernel the library runs for the gate/up GEMM of this shape (the library picks
-    the weight-streaming kernel when groups average at most 10 rows, else the MFMA tile kernel with
-    64-row tiles up to 56 rows per group on average (64 for a single group) and 128-row tiles
-    beyond; the template argument after the epilogue says whether the scales are powers of two)."""
+    the weight-streaming kernel when groups average at most 10 rows, its 32-row variant up to 18,
+    else the MFMA tile kernel with 64-row tiles up to 56 rows per group on average (64 for a single
+    group) and 128-row tiles beyond; the template argument after the epilogue says whether the
+    scales are powers of two)."""
     groups = shape.n_experts if shape.n_experts else 1
     rows = shape.tokens * (shape.top_k if shape.n_experts else 1) // groups
     scaled = "true" if ue8m0 else "false"
     if rows <= 10:
         return f"stream_gemm_kernel<2, 2, 6, 2, {scaled}, true>"
+    if rows <= 18:
+        return f"stream_gemm2_kernel<2, 2, 3, 2, {scaled}, true>"
     mt = 2 if rows <= (56 if groups > 1 else 64) else 4
     return f"mfma_gemm_kernel<2, 4, {mt}, 2, {scaled}>"
 

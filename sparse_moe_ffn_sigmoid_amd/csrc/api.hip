@@ -392,7 +392,7 @@ int fp8_grouped_gemm_blockscaled(const uint8_t* a_q, const float* a_s, const int
   }
   GemmArgs args{};
   GemmSeg& sg = args.seg[1];
-  const int bm = gemm_pick_bm(M_max, G);
+  const int bm = gemm_pick_bm(M_max, G, epilogue == MOE_EPI_SWIGLU_QUANT);
   sg.a_q = a_q;
   sg.a_s = a_s;
   sg.a_gather = a_gather;
@@ -625,7 +625,9 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
   float* h_s = reinterpret_cast<float*>(at(L.h_s));
   uint8_t* hs_q = at(L.hs_q);
   float* hs_s = reinterpret_cast<float*>(at(L.hs_s));
-  const int bm = routed ? gemm_pick_bm(n_assign, E) : gemm_pick_bm(T, 1);
+  // tile rows of the gate/up GEMM (bm) and of the down GEMM (bm_dn)
+  const int bm = routed ? gemm_pick_bm(n_assign, E, true) : gemm_pick_bm(T, 1, true);
+  const int bm_dn = routed ? gemm_pick_bm(n_assign, E, false) : gemm_pick_bm(T, 1, false);
   GemmArgs up{};
   if (cfg->n_shared) {
     GemmSeg& g0 = up.seg[0];
@@ -680,7 +682,7 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
     g0.b_s = w->sh_w2_s;
     g0.G = 1;
     g0.m_rows = T;
-    g0.m_tiles = (T + bm - 1) / bm;
+    g0.m_tiles = (T + bm_dn - 1) / bm_dn;
     g0.N = d;
     g0.K = Ws;
     g0.out = routed ? (void*)y_shared : (void*)out;
@@ -697,14 +699,14 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
     g1.bs_stride = (long long)(d / 128) * (W / 128);
     g1.offsets = offsets;
     g1.G = E;
-    g1.m_tiles = (int)((n_assign + (long)E * (bm - 1)) / bm);
+    g1.m_tiles = (int)((n_assign + (long)E * (bm_dn - 1)) / bm_dn);
     g1.N = d;
     g1.K = W;
     g1.out = y_sorted;
     g1.ld_out = d;
     g1.pow2_scales = pow2;
   }
-  HIP_TRY(launch_grouped_gemm(dn, epi, bm, s), "down GEMM");
+  HIP_TRY(launch_grouped_gemm(dn, epi, bm_dn, s), "down GEMM");
   HIP_TRY(mark(4), "event");
   if (routed)
     HIP_TRY(launch_combine(y_sorted, assign_pos, tw, cfg->n_shared ? y_shared : nullptr, T, k, d, out, s), "combine");

@@ -228,14 +228,18 @@ __device__ bool find_work(const GemmArgs& args, int bm, int ny0, int ny1, int& s
 // Launch bounds: the FP8 kernels with power-of-two scales (NB = 1, SCALED) ask for 3 waves per SIMD;
 // left alone the compiler gave them 208 registers (2 waves), and the down GEMM at decode ran 0.498
 // instead of 0.486 ms.
-template <int NB, int NTW, int P, int EPI, bool SCALED, bool NFAST>
-__global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_kernel(const GemmArgs args) {
+// MB: 16-row blocks per workgroup (1 or 2).  With 2, each streamed B fragment serves both row
+// blocks (converted once per block for the exact path), so a group of up to 32 rows streams its
+// weights once.
+template <int NB, int NTW, int P, int EPI, bool SCALED, bool NFAST, int MB>
+__device__ __forceinline__ void stream_gemm_body(const GemmArgs& args) {
   constexpr int NF = NB * NTW;                 // B fragments per lane per K block
   constexpr int CW = 16 * NTW;                 // columns per wave in each B block
   static_assert(EPI != kEpiSwiglu || NTW % 2 == 0, "the SwiGLU epilogue encodes h in pairs");
+  static_assert(MB == 1 || MB == 2, "one or two row blocks");
   constexpr bool kExact = EPI == kEpiSwiglu;
-  __shared__ float red[4][16];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[16 * 128];
+  __shared__ float red[4][16 * MB];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[16 * MB * 128];
 
   // wave index made wave-uniform: the MFMAs below sit under branches on it, and an MFMA writes
   // every lane whatever EXEC holds, so those branches must be scalar
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_
     }
   }
   int si, g, m0, m_end;
-  if (!find_tile(args, 16, tm, si, g, m0, m_end)) return;
+  if (!find_tile(args, 16 * MB, tm, si, g, m0, m_end)) return;
   const GemmSeg& s0 = args.seg[0];
   const GemmSeg& s1 = args.seg[1];
   const int K = si ? s1.K : s0.K, nkb = K >> 7;
@@ -279,10 +283,16 @@ __global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_
   const uint8_t* const bq = (si ? s1.b_q : s0.b_q) + (long long)g * (si ? s1.b_stride : s0.b_stride);
   const float* const bs = (si ? s1.b_s : s0.b_s) + (long long)g * (si ? s1.bs_stride : s0.bs_stride);
 
-  const int my_m = m0 + r16 < m_end ? m0 + r16 : m0;
-  const long src = gat ? (long)gat[my_m] : (long)my_m;
-  const uint8_t* a_ptr = a_q + src * K + 16 * q;
-  const float* sa_ptr = a_s + src * nkb;
+  // row block b: lane l loads row 16 b + l % 16 (rows past the group's end repeat row m0)
+  const uint8_t* a_ptr[MB];
+  const float* sa_ptr[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int my_m = m0 + 16 * b + r16 < m_end ? m0 + 16 * b + r16 : m0;
+    const long src = gat ? (long)gat[my_m] : (long)my_m;
+    a_ptr[b] = a_q + src * K + 16 * q;
+    sa_ptr[b] = a_s + src * nkb;
+  }
   const uint8_t* b_ptr[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
@@ -294,24 +304,28 @@ __global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) sb_ptr[nb] = bs + (long)((nb * half + (wave_live ? ncol0 : 0)) >> 7) * nkb;
 
-  u32x4 al[P], ah[P], bl[P][NF], bh[P][NF];
-  float sav[P], sbv[P][NB];
+  u32x4 al[P][MB], ah[P][MB], bl[P][NF], bh[P][NF];
+  float sav[P][MB], sbv[P][NB];
 #define STREAM_LOAD(p_, kb_)                                                                 \
   {                                                                                          \
     const int ko_ = (kb_) << 7;                                                              \
-    al[p_] = *reinterpret_cast<const u32x4*>(a_ptr + ko_);                                   \
-    ah[p_] = *reinterpret_cast<const u32x4*>(a_ptr + ko_ + 64);                              \
+    _Pragma("unroll") for (int b = 0; b < MB; ++b) {                                        \
+      al[p_][b] = *reinterpret_cast<const u32x4*>(a_ptr[b] + ko_);                           \
+      ah[p_][b] = *reinterpret_cast<const u32x4*>(a_ptr[b] + ko_ + 64);                      \
+    }                                                                                        \
     _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                        \
       bl[p_][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_ptr[f] + (long)(kb_) * 2048));        \
       bh[p_][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_ptr[f] + (long)(kb_) * 2048 + 1024)); \
     }                                                                                        \
-    sav[p_] = sa_ptr[kb_];                                                                   \
+    _Pragma("unroll") for (int b = 0; b < MB; ++b) sav[p_][b] = sa_ptr[b][kb_];             \
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) sbv[p_][nb] = sb_ptr[nb][kb_];        \
   }
 
-  v4f acc[NF];
+  v4f acc[MB][NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[b][f] = v4f{0.f, 0.f, 0.f, 0.f};
   if (wave_live) {
 #pragma unroll
     for (int p = 0; p < P; ++p)
@@ -321,73 +335,76 @@ __global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_
       for (int p = 0; p < P; ++p) {
         const int kb = kb0 + p;
         if (kb < nkb) {
-          const v8i af = v8i{(int)al[p].x, (int)al[p].y, (int)al[p].z, (int)al[p].w,
-                             (int)ah[p].x, (int)ah[p].y, (int)ah[p].z, (int)ah[p].w};
-          if constexpr (SCALED) {
-            // power-of-two scales: applied exactly by the bf16 conversion (exact path) or as the
-            // FP8 MFMA's E8M0 scale operands, so the MFMA accumulates straight into acc (this lane's
-            // A row, r16, has scale sav[p]; its B column, of block f / NTW, sbv[p][f / NTW])
-            if constexpr (kExact) {
-              v8bf ab[4];
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-                ab[j] = e4m3x8_to_bf16_scaled((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1], sav[p]);
+          for (int b = 0; b < MB; ++b) {
+            const v8i af = v8i{(int)al[p][b].x, (int)al[p][b].y, (int)al[p][b].z, (int)al[p][b].w,
+                               (int)ah[p][b].x, (int)ah[p][b].y, (int)ah[p][b].z, (int)ah[p][b].w};
+            if constexpr (SCALED) {
+              // power-of-two scales: applied exactly by the bf16 conversion (exact path) or as the
+              // FP8 MFMA's E8M0 scale operands, so the MFMA accumulates straight into acc (this lane's
+              // A row, r16 of block b, has scale sav[p][b]; its B column, of block f / NTW, sbv[p][f / NTW])
+              if constexpr (kExact) {
+                v8bf ab[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  ab[j] = e4m3x8_to_bf16_scaled((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1], sav[p][b]);
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                  const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                      (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                  const float sbf = sbv[p][f / NTW];
+#pragma unroll
+                  for (int j = 0; j < 4; ++j)
+                    acc[b][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ab[j], e4m3x8_to_bf16_scaled((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1], sbf), acc[b][f],
+                        0, 0, 0);
+                }
+              } else {
+                const int ea = e8m0_of(sav[p][b]);
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                  const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                      (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                  acc[b][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, acc[b][f], 0, 0, 0, ea, 0,
+                                                                               e8m0_of(sbv[p][f / NTW]));
+                }
+              }
+            } else {
+              v4f part[NF];
+              if constexpr (kExact) {
+                v8bf ab[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ab[j] = e4m3x8_to_bf16((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1]);
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                  const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                      (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                  v4f t = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int j = 0; j < 4; ++j)
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ab[j], e4m3x8_to_bf16((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1]), t, 0, 0, 0);
+                  part[f] = t;
+                }
+              } else {
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                  const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
+                                      (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
+                  part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                             0, 0, 0, 0);
+                }
+              }
+              // row 4q+i's activation scale sits in lane 4q+i
+              float srow[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) srow[i] = __shfl(sav[p][b], 4 * q + i);
 #pragma unroll
               for (int f = 0; f < NF; ++f) {
-                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
-                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
                 const float sbf = sbv[p][f / NTW];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                  acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      ab[j], e4m3x8_to_bf16_scaled((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1], sbf), acc[f], 0, 0,
-                      0);
+                for (int i = 0; i < 4; ++i) acc[b][f][i] = fmaf(part[f][i], srow[i] * sbf, acc[b][f][i]);
               }
-            } else {
-              const int ea = e8m0_of(sav[p]);
-#pragma unroll
-              for (int f = 0; f < NF; ++f) {
-                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
-                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
-                acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, acc[f], 0, 0, 0, ea, 0,
-                                                                          e8m0_of(sbv[p][f / NTW]));
-              }
-            }
-          } else {
-            v4f part[NF];
-            if constexpr (kExact) {
-              v8bf ab[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) ab[j] = e4m3x8_to_bf16((uint32_t)af[2 * j], (uint32_t)af[2 * j + 1]);
-#pragma unroll
-              for (int f = 0; f < NF; ++f) {
-                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
-                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
-                v4f t = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                  t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      ab[j], e4m3x8_to_bf16((uint32_t)bfr[2 * j], (uint32_t)bfr[2 * j + 1]), t, 0, 0, 0);
-                part[f] = t;
-              }
-            } else {
-#pragma unroll
-              for (int f = 0; f < NF; ++f) {
-                const v8i bfr = v8i{(int)bl[p][f].x, (int)bl[p][f].y, (int)bl[p][f].z, (int)bl[p][f].w,
-                                    (int)bh[p][f].x, (int)bh[p][f].y, (int)bh[p][f].z, (int)bh[p][f].w};
-                part[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                                           0, 0, 0);
-              }
-            }
-            // row 4q+i's activation scale sits in lane 4q+i
-            float srow[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) srow[i] = __shfl(sav[p], 4 * q + i);
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-              const float sbf = sbv[p][f / NTW];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[f][i] = fmaf(part[f][i], srow[i] * sbf, acc[f][i]);
             }
           }
           if (kb + P < nkb) STREAM_LOAD(p, kb + P);
@@ -402,38 +419,44 @@ __global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_
   const int ld_out = si ? s1.ld_out : s0.ld_out;
   const int32_t* const dst_row = si ? s1.dst_row : s0.dst_row;
   const float* const row_w = si ? s1.row_w : s0.row_w;
-  // lane holds rows m0 + 4q + i, columns ncol0 + 16 j + r16 of each B block
+  // lane holds rows m0 + 16 b + 4q + i, columns ncol0 + 16 j + r16 of each B block
   if constexpr (EPI == kEpiSwiglu) {
-    float h[NTW][4];
+    float h[MB][NTW][4];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[j][i] = swiglu(acc[j][i], acc[NTW + j][i]);
+      for (int j = 0; j < NTW; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = 0.0f;
+        for (int i = 0; i < 4; ++i) h[b][j][i] = swiglu(acc[b][j][i], acc[b][NTW + j][i]);
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) mx = fmaxf(mx, fabsf(h[j][i]));
-      mx = group_max<16>(mx);
-      if (r16 == 0) red[wave][4 * q + i] = mx;
-    }
-    __syncthreads();
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * q + i;
-      const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-      const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
-      const float inv = 1.0f / sc;                // x * inv is within an ulp of x / sc (equal for power-of-two sc)
+      for (int i = 0; i < 4; ++i) {
+        float mx = 0.0f;
 #pragma unroll
-      for (int j = 0; j < NTW; j += 2) {
-        const uint32_t c2 = e4m3_encode2(h[j][i] * inv, h[j + 1][i] * inv);
-        stage[r * 128 + wave * CW + 16 * j + r16] = (uint8_t)c2;
-        stage[r * 128 + wave * CW + 16 * (j + 1) + r16] = (uint8_t)(c2 >> 8);
+        for (int j = 0; j < NTW; ++j) mx = fmaxf(mx, fabsf(h[b][j][i]));
+        mx = group_max<16>(mx);
+        if (r16 == 0) red[wave][16 * b + 4 * q + i] = mx;
       }
-      if (wave == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + (nbase >> 7)] = sc;
-    }
     __syncthreads();
-    if (tid < 128) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * b + 4 * q + i;
+        const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+        const float sc = tile_scale(amax, (si ? s1.pow2_scales : s0.pow2_scales) != 0);
+        const float inv = 1.0f / sc;              // x * inv is within an ulp of x / sc (equal for power-of-two sc)
+#pragma unroll
+        for (int j = 0; j < NTW; j += 2) {
+          const uint32_t c2 = e4m3_encode2(h[b][j][i] * inv, h[b][j + 1][i] * inv);
+          stage[r * 128 + wave * CW + 16 * j + r16] = (uint8_t)c2;
+          stage[r * 128 + wave * CW + 16 * (j + 1) + r16] = (uint8_t)(c2 >> 8);
+        }
+        if (wave == 0 && r16 == 0 && m0 + r < m_end) out_s[(long)(m0 + r) * (half >> 7) + (nbase >> 7)] = sc;
+      }
+    __syncthreads();
+    if (tid < 128 * MB) {
       const int r = tid >> 3, c = tid & 7;
       if (m0 + r < m_end)
         *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(out) + (long)(m0 + r) * ld_out + nbase + c * 16) =
@@ -442,25 +465,38 @@ __global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_
   } else {
     if (!wave_live) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 4 * q + i;
-      if (m >= m_end) continue;
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int n = ncol0 + 16 * f + r16;
-        const float val = acc[f][i];
-        if constexpr (EPI == kEpiF32) {
-          reinterpret_cast<float*>(out)[(long)m * ld_out + n] = val;
-        } else if constexpr (EPI == kEpiBf16) {
-          reinterpret_cast<uint16_t*>(out)[(long)m * ld_out + n] = f32_to_bf16_rne(val);
-        } else {
-          const long dst = dst_row ? (long)dst_row[m] : (long)m;
-          const float wgt = row_w ? row_w[m] : 1.0f;
-          atomicAdd(reinterpret_cast<float*>(out) + dst * ld_out + n, wgt * val);
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * b + 4 * q + i;
+        if (m >= m_end) continue;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int n = ncol0 + 16 * f + r16;
+          const float val = acc[b][f][i];
+          if constexpr (EPI == kEpiF32) {
+            reinterpret_cast<float*>(out)[(long)m * ld_out + n] = val;
+          } else if constexpr (EPI == kEpiBf16) {
+            reinterpret_cast<uint16_t*>(out)[(long)m * ld_out + n] = f32_to_bf16_rne(val);
+          } else {
+            const long dst = dst_row ? (long)dst_row[m] : (long)m;
+            const float wgt = row_w ? row_w[m] : 1.0f;
+            atomicAdd(reinterpret_cast<float*>(out) + dst * ld_out + n, wgt * val);
+          }
         }
       }
-    }
   }
+}
+
+template <int NB, int NTW, int P, int EPI, bool SCALED, bool NFAST>
+__global__ __launch_bounds__(256, (SCALED && NB == 1) ? 3 : 1) void stream_gemm_kernel(const GemmArgs args) {
+  stream_gemm_body<NB, NTW, P, EPI, SCALED, NFAST, 1>(args);
+}
+
+// The same with 32-row tiles (two row blocks per workgroup), used for the gate/up GEMM.
+template <int NB, int NTW, int P, int EPI, bool SCALED, bool NFAST>
+__global__ __launch_bounds__(256) void stream_gemm2_kernel(const GemmArgs args) {
+  stream_gemm_body<NB, NTW, P, EPI, SCALED, NFAST, 2>(args);
 }
 
 // The launch's scale format: power-of-two scales when its segments say so (the forward sets both
@@ -469,7 +505,18 @@ static bool gemm_pow2(const GemmArgs& args) {
   return (args.seg[1].m_tiles > 0 ? args.seg[1] : args.seg[0]).pow2_scales != 0;
 }
 
-static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
+template <int MB, int PG, int PD>
+static hipError_t launch_stream_mb(const GemmArgs& args, int epi, hipStream_t st);
+
+// MB = 1 (groups of up to 16 rows per tile): the decode kernels; MB = 2: 32-row tiles, for the
+// gate/up GEMM only (the FP8 down GEMM measured faster on the 64-row LDS tiles there).
+static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st, int mb) {
+  return mb == 2 ? launch_stream_mb<2, 3, 3>(args, epi, st) : launch_stream_mb<1, 6, 4>(args, epi, st);
+}
+
+// PG, PD: K blocks in flight per wave in the gate/up (SwiGLU) and the other kernels.
+template <int MB, int PG, int PD>
+static hipError_t launch_stream_mb(const GemmArgs& args, int epi, hipStream_t st) {
   const int mt = args.seg[0].m_tiles + args.seg[1].m_tiles;
   if (mt == 0) return hipSuccess;
   const bool swiglu = epi == kEpiSwiglu;
@@ -485,22 +532,31 @@ static hipError_t launch_stream(const GemmArgs& args, int epi, hipStream_t st) {
   }
   if (ny == 0) return hipSuccess;
   const dim3 grid(ny, mt), grid_m(mt, ny);
-  if (gemm_pow2(args)) {
-    switch (epi) {
-      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, true, true><<<grid, 256, 0, st>>>(args); break;
-      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, true, false><<<grid_m, 256, 0, st>>>(args); break;
-      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, true, false><<<grid_m, 256, 0, st>>>(args); break;
-      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, true, false><<<grid_m, 256, 0, st>>>(args); break;
-    }
+  if constexpr (MB == 2) {                        // the gate/up (SwiGLU) GEMM only
+    if (epi != kEpiSwiglu) return hipErrorInvalidValue;
+    if (gemm_pow2(args)) stream_gemm2_kernel<2, 2, PG, kEpiSwiglu, true, true><<<grid, 256, 0, st>>>(args);
+    else stream_gemm2_kernel<2, 2, PG, kEpiSwiglu, false, true><<<grid, 256, 0, st>>>(args);
+    return hipGetLastError();
   } else {
-    switch (epi) {
-      case kEpiSwiglu: stream_gemm_kernel<2, 2, 6, kEpiSwiglu, false, true><<<grid, 256, 0, st>>>(args); break;
-      case kEpiF32: stream_gemm_kernel<1, 2, 4, kEpiF32, false, false><<<grid_m, 256, 0, st>>>(args); break;
-      case kEpiBf16: stream_gemm_kernel<1, 2, 4, kEpiBf16, false, false><<<grid_m, 256, 0, st>>>(args); break;
-      default: stream_gemm_kernel<1, 2, 4, kEpiScatter, false, false><<<grid_m, 256, 0, st>>>(args); break;
+#define STREAM_LAUNCH(NB_, P_, EPI_, SC_, NF_, G_) stream_gemm_kernel<NB_, 2, P_, EPI_, SC_, NF_><<<G_, 256, 0, st>>>(args)
+    if (gemm_pow2(args)) {
+      switch (epi) {
+        case kEpiSwiglu: STREAM_LAUNCH(2, PG, kEpiSwiglu, true, true, grid); break;
+        case kEpiF32: STREAM_LAUNCH(1, PD, kEpiF32, true, false, grid_m); break;
+        case kEpiBf16: STREAM_LAUNCH(1, PD, kEpiBf16, true, false, grid_m); break;
+        default: STREAM_LAUNCH(1, PD, kEpiScatter, true, false, grid_m); break;
+      }
+    } else {
+      switch (epi) {
+        case kEpiSwiglu: STREAM_LAUNCH(2, PG, kEpiSwiglu, false, true, grid); break;
+        case kEpiF32: STREAM_LAUNCH(1, PD, kEpiF32, false, false, grid_m); break;
+        case kEpiBf16: STREAM_LAUNCH(1, PD, kEpiBf16, false, false, grid_m); break;
+        default: STREAM_LAUNCH(1, PD, kEpiScatter, false, false, grid_m); break;
+      }
     }
+#undef STREAM_LAUNCH
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1078,7 +1134,8 @@ static hipError_t launch_mfma(const GemmArgs& args, int epi, hipStream_t st) {
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st) {
   switch (bm) {
-    case 16: return launch_stream(args, epi, st);
+    case 16: return launch_stream(args, epi, st, 1);
+    case 32: return launch_stream(args, epi, st, 2);
     case 64: return launch_mfma<2>(args, epi, st);
     default: return launch_mfma<4>(args, epi, st);
   }
@@ -1091,10 +1148,14 @@ hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_
 // their weights once per 16-row tile; 64-row tiles beat 32-row ones everywhere (T = 1024: 2.28
 // against 3.28 ms) and 128-row ones up to 56 rows per expert (T = 1536: 2.48 against 2.53;
 // T = 2048, 64 rows: 3.0 against 2.75).  A single group (the dense layer) has exactly its rows,
-// so 64-row tiles hold it up to 64.
-int gemm_pick_bm(long rows_upper, int groups) {
+// so 64-row tiles hold it up to 64.  The gate/up GEMM (SwiGLU epilogue) takes the 32-row streaming
+// tiles from 11 to 18 rows: T = 352: 1.20 against 1.28 ms for the 64-row tiles, T = 512: 1.24
+// against 1.30, T = 576: 1.28 against 1.30, T = 640: 1.32 against 1.31; the FP8 down GEMM ran
+// slower on them at every size (T = 352: 0.72 against 0.66 ms) and keeps the 64-row tiles.
+int gemm_pick_bm(long rows_upper, int groups, bool swiglu) {
   const long avg = groups > 0 ? rows_upper / groups : rows_upper;
   if (avg <= 10) return 16;
+  if (swiglu && avg <= 18) return 32;
   if (avg <= (groups > 1 ? 56 : 64)) return 64;
   return 128;
 }

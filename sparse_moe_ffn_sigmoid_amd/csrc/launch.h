@@ -79,7 +79,7 @@ hipError_t launch_wgrad(const uint8_t* a_t, const float* a_ts, const uint8_t* b_
 // Grouped block-scaled GEMM.  bm = rows per tile (16, 32, 64 or 128); the
 // caller sets each segment's m_tiles for that bm.
 hipError_t launch_grouped_gemm(const GemmArgs& args, int epi, int bm, hipStream_t st);
-int gemm_pick_bm(long rows_upper, int groups);
+int gemm_pick_bm(long rows_upper, int groups, bool swiglu);
 
 // Device-data checks (validate.hip).  Each runs on `st`, synchronises it and sets *first_bad to
 // the smallest offending element index, or -1 when every element passes.

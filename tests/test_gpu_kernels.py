@@ -305,6 +305,10 @@ def _gemm_case(seed, M_groups, N, K, gather_rows=None):
 # Group sizes pick the kernel: <= 10 rows on average the weight-streaming kernel, else the LDS
 # tile kernel with 64- or 128-row tiles; a group's partial last tile runs the kernel's
 # partial-tile path (row blocks past the group's end skipped).
+def _sizes(seed, G, lo, hi):
+    return [int(v) for v in np.random.default_rng(seed).integers(lo, hi + 1, G)]
+
+
 GEMM_CASES = [
     ([16], 128, 128, None),
     ([9], 128, 128, None),                           # weight-streaming path, one group
@@ -317,11 +321,9 @@ GEMM_CASES = [
     ([130, 0, 161, 95, 170, 224], 384, 640, None),   # partial second tiles of 2, 33, 42 and 96 rows
     ([150, 120, 118], 512, 256, 200),                # gathered rows, partial tiles of 22..120 rows, two K blocks
     ([3, 9, 0, 14, 1], 384, 256, 40),                # weight-streaming path: three 128-column workgroups
+    ([17, 32, 0, 25, 9], 256, 384, None),            # 11-18 rows per group (the SwiGLU GEMM's 32-row streaming tiles)
+    (_sizes(10, 48, 6, 30), 384, 256, 200),          # the same, gathered rows
 ]
-
-
-def _sizes(seed, G, lo, hi):
-    return [int(v) for v in np.random.default_rng(seed).integers(lo, hi + 1, G)]
 
 
 # More than 64 groups: each lane of the tile lookup then scans several groups (G = 65 leaves the
@@ -376,7 +378,8 @@ def test_grouped_gemm_bf16_and_scatter(mg):
                                          ([1000], 128, 384, False), ([40, 90], 128, 256, True),
                                          ([130, 0, 75, 200], 256, 768, False), ([66, 128], 128, 128, False),
                                          ([140, 0, 200, 161], 256, 768, False), ([120, 130], 128, 128, False),
-                                         ([5, 0, 12, 16, 3], 384, 256, False),
+                                         ([5, 0, 12, 16, 3], 384, 256, False), ([20, 0, 31, 12], 256, 384, False),
+                                         (_sizes(11, 40, 4, 28), 128, 256, False),
                                          (_sizes(6, 80, 0, 60), 128, 256, False),
                                          (_sizes(7, 300, 0, 10), 256, 128, False)])
 def test_grouped_gemm_swiglu_quant(mg, W, K, wide):
