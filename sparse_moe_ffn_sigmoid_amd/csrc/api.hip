@@ -298,7 +298,7 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, in
             cfg->hidden);
     REQUIRE(cfg->n_experts % 16 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "n_experts %d not a multiple of 16", cfg->n_experts);
     REQUIRE(aligned(x, 16) && aligned(w_router, 16), MOE_ERR_INVALID_ARG, "x / w_router not 16-byte aligned");
-    HIP_TRY(launch_router(x, w_router, T, cfg->n_experts, cfg->hidden, scores, nullptr, s), "router");
+    HIP_TRY(launch_router(x, w_router, T, cfg->n_experts, cfg->hidden, scores, nullptr, 0, s), "router");
   }
   HIP_TRY(launch_route(scores, bias, T, cfg->n_experts, cfg->top_k, cfg->n_group, cfg->topk_group, cfg->group_score,
                        cfg->routed_scale, topk_idx, topk_w, s),
@@ -604,11 +604,10 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
     float* sc = scores ? scores : reinterpret_cast<float*>(at(L.scores));
     int32_t* ti = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(L.topk_idx));
     if (!(flags & MOE_ROUTE_SCORES_GIVEN)) {
-      // the router's partial logits (small batches) borrow the down GEMM's output rows, unused until then
+      // the router's partial logits (K split over workgroups) borrow the down GEMM's output rows, unused until then
       // (the split's last step stores the scores 16 bytes at a time: a caller's scores buffer must allow it)
-      float* part = router_partial_floats(T, E) <= (size_t)n_assign * (size_t)d && aligned(sc, 16)
-                        ? reinterpret_cast<float*>(at(L.y_sorted)) : nullptr;
-      HIP_TRY(launch_router(xin, w->w_router, T, E, d, sc, part, s), "router");
+      float* part = aligned(sc, 16) ? reinterpret_cast<float*>(at(L.y_sorted)) : nullptr;
+      HIP_TRY(launch_router(xin, w->w_router, T, E, d, sc, part, (size_t)n_assign * (size_t)d, s), "router");
     }
     HIP_TRY(launch_route(sc, w->bias, T, E, k, cfg->n_group, cfg->topk_group, cfg->group_score, cfg->routed_scale, ti,
                          tw, s),

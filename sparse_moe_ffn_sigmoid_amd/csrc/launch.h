@@ -48,10 +48,10 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
 hipError_t launch_bias_update(const int32_t* topk_idx, long n, int E, float gamma, float* bias, int32_t* counts,
                               hipStream_t st);
 hipError_t launch_pack(const uint8_t* src, int G, int N, int K, uint8_t* dst, hipStream_t st);
-// part: NULL, or a buffer of router_partial_floats(T, E) floats for the small-batch K split
+// part: NULL, or a buffer of part_floats floats for partial logits (the K splits use it when it
+// holds their T * E * splits floats; scores must then be 16-byte aligned)
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, float* part,
-                         hipStream_t st);
-size_t router_partial_floats(int T, int E);
+                         size_t part_floats, hipStream_t st);
 hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,
                         float routed_scale, int32_t* topk_idx, float* topk_w, hipStream_t st);
 size_t permute_scratch_bytes(int n, int E);

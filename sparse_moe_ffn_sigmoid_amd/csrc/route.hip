@@ -1,6 +1,7 @@
 // Gating kernels: router GEMM + sigmoid, and group-limited top-k selection
 // (onlylabs "DeepSeek v3 and R1 Model Architecture", "Local Balanced Routing to
 // Experts": token-to-expert affinity plus a routing-only bias term).
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -110,6 +111,128 @@ __global__ __launch_bounds__(64 * NW) void router_splitk_kernel(const uint16_t* 
       }
     }
   }
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed (lgkmcnt(0)), leaving its global
+// loads in flight (__syncthreads() would also wait for every one of them).
+__device__ __forceinline__ void router_lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);           // vmcnt 63 and expcnt 7: no wait; lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Large batches: a workgroup of 8 waves covers 128 tokens x 256 experts, so each token row is read
+// once and each router weight row once per 128 tokens; the hidden dimension goes through LDS in
+// chunks of 64 (A 16 KB + B 32 KB per stage, two stages), each chunk's loads issued two chunks
+// ahead into registers and written to LDS one chunk ahead.  Rows are stored as 128-byte lines with
+// the 16-byte piece index XORed by row % 8, so a fragment read (16 rows, one piece) spreads over
+// the banks.  Wave (wm, wn) computes tokens 64 wm .. +63 x experts 64 wn .. +63.  gridDim.z > 1
+// splits the chunks into near-equal ranges over workgroups (raw partial logits to
+// out[z][T][E], added in order of z by router_finish_kernel); with one range the kernel applies
+// the sigmoid itself.  Every output is one MFMA chain in chunk order: deterministic.
+__global__ __launch_bounds__(512) void router_lds_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w, int T, int E, int D,
+                                                         float* __restrict__ out) {
+  constexpr int A_BYTES = 128 * 128, STAGE = A_BYTES + 256 * 128;
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave & 1, wn = wave >> 1;
+  const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 256;
+  const int z = blockIdx.z, nz = gridDim.z, nch = D >> 6;
+  const int c0 = (nch * z) / nz, nk = (nch * (z + 1)) / nz - c0;   // >= 1: the host keeps nz <= nch
+  // this thread's 16-byte pieces of a chunk: A (x) pieces tid and tid + 512 of 1024 (8 per row),
+  // B (router weight) pieces tid + 512 i of 2048; sources clamp rows past the batch to its last
+  const uint16_t* a_src[2];
+  int a_dst[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + 512 * i, r = p >> 3, c = p & 7;
+    a_src[i] = x + (long)min(t0 + r, T - 1) * D + (long)c0 * 64 + 8 * c;
+    a_dst[i] = r * 128 + 16 * (c ^ (r & 7));
+  }
+  const uint16_t* b_src[4];
+  int b_dst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 512 * i, r = p >> 3, c = p & 7;
+    b_src[i] = w + (long)(e0 + r) * D + (long)c0 * 64 + 8 * c;
+    b_dst[i] = A_BYTES + r * 128 + 16 * (c ^ (r & 7));
+  }
+  // chunk j of this range into registers (past the range: its last chunk again, never stored)
+  auto gload = [&](int j, u32x4 (&ra)[2], u32x4 (&rb)[4]) __attribute__((always_inline)) {
+    const long off = (long)min(j, nk - 1) * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + off);
+  };
+  auto swrite = [&](uint8_t* st, const u32x4 (&ra)[2], const u32x4 (&rb)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(st + a_dst[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(st + b_dst[i]) = rb[i];
+  };
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the lane's fragment rows: token 64 wm + 16 i + r16, expert 64 wn + 16 j + r16 (row % 8 = r16 % 8)
+  const int swz = r16 & 7;
+  auto compute = [&](const uint8_t* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {               // two 32-wide K steps per chunk
+      const int piece = 16 * ((4 * s + q) ^ swz);
+      v8bf a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v8bf*>(st + (64 * wm + 16 * i + r16) * 128 + piece);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const v8bf*>(st + A_BYTES + (64 * wn + 16 * j + r16) * 128 + piece);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  u32x4 ra0[2], rb0[4], ra1[2], rb1[4];
+  gload(0, ra0, rb0);
+  gload(1, ra1, rb1);
+  swrite(lds0, ra0, rb0);
+  gload(2, ra0, rb0);
+  router_lds_barrier();
+  // at the top of each round: stage 0 holds chunk c, registers set 1 chunk c + 1 and set 0 chunk
+  // c + 2 (both in flight)
+  int c = 0;
+  for (; c + 2 <= nk; c += 2) {
+    compute(lds0);
+    swrite(lds1, ra1, rb1);
+    gload(c + 3, ra1, rb1);
+    router_lds_barrier();
+    compute(lds1);
+    swrite(lds0, ra0, rb0);
+    gload(c + 4, ra0, rb0);
+    router_lds_barrier();
+  }
+  if (c < nk) compute(lds0);                    // an odd count: the last chunk
+  // lane holds tokens 4q .. 4q + 3 of token tile i, expert r16 of expert tile j
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = t0 + 64 * wm + 16 * i + 4 * q + r;
+      if (tt < T) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = e0 + 64 * wn + 16 * j + r16;
+          const float v = acc[i][j][r];
+          if (nz > 1) out[((long)z * T + tt) * E + e] = v;
+          else out[(long)tt * E + e] = 1.0f / (1.0f + expf(-v));
+        }
+      }
+    }
 }
 
 // Wave-wide maximum of a 64-bit key, every lane receiving it: DPP exchanges within each row of 16
@@ -316,21 +439,36 @@ __global__ __launch_bounds__(256) void router_finish_kernel(const float* __restr
   reinterpret_cast<v4f*>(scores)[i] = o;
 }
 
-// Batches of up to 1024 tokens: 16 x 16 tiles of 16 waves (at T = 640 the route + permutation
-// stage took 68 against 80 us with the 64 x 64 tiles, equal at 1024, 80 against 109 us at 1536
-// for the 64 x 64 tiles); up to 512 tokens, with a partial-logit buffer of kRouterSplit * T * E
-// floats (the forward lends one) and a hidden dimension of at least 4096, also split 4 ways over
-// the hidden dimension (at T = 64: 256 workgroups instead of 64).
-constexpr int kRouterSplit = 4;
+// Up to 512 tokens: 16 x 16 tiles of 16 waves; with a partial-logit buffer of kRouterSplit * T * E
+// floats (the forward lends one) and a hidden dimension of at least 4096 the hidden dimension is
+// also split 4 ways (at T = 64: 256 workgroups instead of 64).  Larger batches with a
+// partial-logit buffer (the forward's) and 256k experts: router_lds_kernel, its K range split over
+// up to 16 workgroups so that the grid fills the chip (T = 4096: 32 token tiles x 8); V3 router,
+// route + permutation stage: T = 1280 0.079 -> 0.050 ms, 4096 0.083 -> 0.067, 16384 0.271 ->
+// 0.134.  Otherwise (moe_route's router, other expert counts) the 16 x 16 tiles up to 1024 tokens
+// (at T = 640 the route + permutation stage took 68 against 80 us with the 64 x 64 tiles, equal
+// at 1024, 80 against 109 us at 1536), then 64 x 64 token x expert tiles.
+constexpr int kRouterSplit = 4, kRouterLdsSplitMax = 16;
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, float* part,
-                         hipStream_t st) {
+                         size_t part_floats, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (T <= 512 && part && D >= 4096) {
+  const long n = (long)T * E;
+  if (T <= 512 && part && D >= 4096 && part_floats >= (size_t)kRouterSplit * n) {
     router_splitk_kernel<16, 1, 1, 8, true><<<dim3((T + 15) / 16, E / 16, kRouterSplit), 1024, 0, st>>>(x, w, T, E, D,
                                                                                                          part);
-    const long n = (long)T * E;
     router_finish_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(part, kRouterSplit, n, scores);
+  } else if (T > 512 && part && E % 256 == 0 && D % 64 == 0) {
+    const int tiles = ((T + 127) / 128) * (E / 256);
+    int nz = std::min(kRouterLdsSplitMax, std::max(1, 256 / tiles));
+    nz = (int)std::min<size_t>((size_t)std::min(nz, D / 64), part_floats / (size_t)n);
+    const dim3 grid((T + 127) / 128, E / 256, nz > 1 ? nz : 1);
+    if (nz > 1) {
+      router_lds_kernel<<<grid, 512, 0, st>>>(x, w, T, E, D, part);
+      router_finish_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(part, nz, n, scores);
+    } else {
+      router_lds_kernel<<<grid, 512, 0, st>>>(x, w, T, E, D, scores);
+    }
   } else if (T <= 1024) {
     router_splitk_kernel<16, 1, 1, 8, false><<<dim3((T + 15) / 16, E / 16), 1024, 0, st>>>(x, w, T, E, D, scores);
   } else if (E % 64 == 0) {
@@ -340,8 +478,6 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int
   }
   return hipGetLastError();
 }
-
-size_t router_partial_floats(int T, int E) { return (size_t)kRouterSplit * (size_t)T * (size_t)E; }
 
 hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,
                         float routed_scale, int32_t* topk_idx, float* topk_w, hipStream_t st) {

@@ -163,6 +163,35 @@ def test_forward_router_scores_split_over_k(T):
     _compare_router_run(layer, xb, got)
 
 
+ROUTER_LDS = synth.MoeShape("router_lds", 22, 1100, 1152, 128, 256, 8, 1, 128, 8, 4)
+
+
+@pytest.mark.parametrize("T,hidden,E,whole", [
+    (700, 1152, 256, True),     # 6 token tiles (the last of 60 tokens), K split 16 ways: 1 or 2 chunks of 64
+    (1100, 1152, 256, True),    # 9 token tiles (the last of 76 tokens), K split 16 ways
+    (1536, 2560, 256, False),   # 12 token tiles, K split 16 ways: 2 or 3 chunks (an odd count's last chunk)
+    (2048, 256, 256, True),     # the split capped by the hidden dimension: 4 ways of one chunk
+    (8192, 256, 1024, False),   # 64 token tiles x 4 expert tiles: no split, the sigmoid in the kernel
+])
+def test_forward_router_scores_large_batch(T, hidden, E, whole):
+    """Batches above 512 tokens with 256k experts: the forward's router stages 128 tokens x 256
+    experts through LDS, its hidden dimension split over workgroups whose partial logits are added
+    in a fixed order.  Every score against the oracle's (the bound of the single-pass router); the
+    layer against the oracle on every token, or on the first and last 128 tokens."""
+    s = dataclasses.replace(ROUTER_LDS, tokens=T, hidden=hidden, n_experts=E)
+    say(f"forward router, LDS-staged: T={T}, hidden {hidden}, E={E}")
+    layer = Layer(s)
+    xb = synth.gen_x(s)
+    got = _run(layer, xb)
+    want = route.sigmoid_scores(route.router_logits(synth.bf16_bits_to_f32(xb),
+                                                    synth.bf16_bits_to_f32(synth.gen_router_w(s))))
+    assert np.abs(got["scores"] - want).max() <= 2e-5
+    toks = None if whole else np.r_[0:128, T - 128:T]
+    _compare_router_run(layer, xb, got, tokens=toks, chunks=4)
+    again = _run(layer, xb)
+    assert np.array_equal(again["scores"], got["scores"]) and np.array_equal(again["out"], got["out"])
+
+
 # ---- V3 shapes, in the benchmark's launch configuration, on sampled tokens ----
 
 @pytest.fixture(scope="module")
@@ -196,6 +225,9 @@ def test_v3_decode_every_token(v3):
 def test_v3_prefill_sampled_tokens(v3, shape):
     say(f"forward {shape.name} T={shape.tokens} (sampled oracle check)")
     xb, got = _v3_run(v3, shape)
+    # every score of the batch (the router's K split at this size) against the oracle's router
+    want = route.sigmoid_scores(route.router_logits(synth.bf16_bits_to_f32(xb), synth.bf16_bits_to_f32(v3.wr_bits)))
+    assert np.abs(got["scores"] - want).max() <= 2e-5
     toks = pick_tokens(got["topk_idx"], 256, 32, shape.cfg_id)
     _compare_router_run(v3, xb, got, tokens=toks, chunks=8)
     v3.bias = None
