@@ -298,7 +298,7 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, in
             cfg->hidden);
     REQUIRE(cfg->n_experts % 16 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "n_experts %d not a multiple of 16", cfg->n_experts);
     REQUIRE(aligned(x, 16) && aligned(w_router, 16), MOE_ERR_INVALID_ARG, "x / w_router not 16-byte aligned");
-    HIP_TRY(launch_router(x, w_router, T, cfg->n_experts, cfg->hidden, scores, nullptr, 0, s), "router");
+    HIP_TRY(launch_router(x, w_router, T, cfg->n_experts, cfg->hidden, scores, nullptr, 0, nullptr, s), "router");
   }
   HIP_TRY(launch_route(scores, bias, T, cfg->n_experts, cfg->top_k, cfg->n_group, cfg->topk_group, cfg->group_score,
                        cfg->routed_scale, topk_idx, topk_w, s),
@@ -584,13 +584,23 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
   float* x_s = reinterpret_cast<float*>(at(L.x_s));
   const bool pow2 = cfg->scale_fmt == MOE_SCALE_UE8M0;
   const uint16_t* xin = x;                      // the rows the router reads
+  const long n_assign = (long)T * k;
+  float* sc = routed ? (scores ? scores : reinterpret_cast<float*>(at(L.scores))) : nullptr;
+  const bool run_router = routed && !(flags & MOE_ROUTE_SCORES_GIVEN);
+  // the router's partial logits (K split over workgroups) borrow the down GEMM's output rows, unused until then
+  // (the split's last step stores the scores 16 bytes at a time: a caller's scores buffer must allow it)
+  float* part = run_router && aligned(sc, 16) ? reinterpret_cast<float*>(at(L.y_sorted)) : nullptr;
+  const size_t part_floats = (size_t)n_assign * (size_t)d;
+  // small batches: x's quantisation rides in the router's finishing kernel (one launch less)
+  const RouterQuant xq{x_q, x_s, pow2};
+  const bool quant_in_router = !w->norm_w && run_router && router_small_split(T, E, d, part, part_floats);
   HIP_TRY(mark(0), "event");
   if (w->norm_w) {
     uint16_t* x_norm = reinterpret_cast<uint16_t*>(at(L.x_norm));
     HIP_TRY(launch_rmsnorm_quant(x, w->norm_w, cfg->norm_eps, T, d, d, x_norm, d, x_q, d, x_s, pow2, s),
             "RMSNorm + quantize x");
     xin = x_norm;
-  } else {
+  } else if (!quant_in_router) {
     HIP_TRY(launch_quant_1x128(x, true, T, d, d, x_q, d, x_s, pow2, s), "quantize x");
   }
   HIP_TRY(mark(1), "event");
@@ -599,16 +609,11 @@ int moe_ffn_forward_stages(const uint16_t* x, int T, const moe_cfg_t* cfg, const
   int32_t* assign_pos = reinterpret_cast<int32_t*>(at(L.assign_pos));
   int32_t* offsets = reinterpret_cast<int32_t*>(at(L.offsets));
   float* tw = topk_w ? topk_w : reinterpret_cast<float*>(at(L.topk_w));
-  const long n_assign = (long)T * k;
   if (routed) {
-    float* sc = scores ? scores : reinterpret_cast<float*>(at(L.scores));
     int32_t* ti = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(L.topk_idx));
-    if (!(flags & MOE_ROUTE_SCORES_GIVEN)) {
-      // the router's partial logits (K split over workgroups) borrow the down GEMM's output rows, unused until then
-      // (the split's last step stores the scores 16 bytes at a time: a caller's scores buffer must allow it)
-      float* part = aligned(sc, 16) ? reinterpret_cast<float*>(at(L.y_sorted)) : nullptr;
-      HIP_TRY(launch_router(xin, w->w_router, T, E, d, sc, part, (size_t)n_assign * (size_t)d, s), "router");
-    }
+    if (run_router)
+      HIP_TRY(launch_router(xin, w->w_router, T, E, d, sc, part, part_floats, quant_in_router ? &xq : nullptr, s),
+              "router");
     HIP_TRY(launch_route(sc, w->bias, T, E, k, cfg->n_group, cfg->topk_group, cfg->group_score, cfg->routed_scale, ti,
                          tw, s),
             "route");

@@ -105,6 +105,54 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
+// 1x128 quantisation of tile `tile` (row-major over rows x cols / 128 tiles) by a 16-lane group,
+// lane `sub` holding 8 consecutive elements (one 16-byte load for bf16, two for fp32; one 8-byte
+// store of codes): amax = max |v|, s = fp32(amax / 448) (correctly rounded division),
+// q = e4m3(fp32(v / s)); an all-zero tile has s = 1.  Every lane of the group must call it (the
+// amax is reduced across the group); a tile index past the end stores nothing.
+template <bool kBf16>
+__device__ __forceinline__ void quant_1x128_tile(const void* __restrict__ x, int rows, int cols, int ld_x,
+                                                 uint8_t* __restrict__ q, int ld_q, float* __restrict__ s, int pow2,
+                                                 long tile, int sub) {
+  const int tpr = cols >> 7;
+  const long ntiles = (long)rows * tpr;
+  const bool valid = tile < ntiles;
+  const long r = valid ? tile / tpr : 0;
+  const int tc = valid ? (int)(tile - r * tpr) : 0;
+  const int c0 = tc * 128 + sub * 8;
+  float v[8];
+  if (valid) {
+    if (kBf16) {
+      const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + r * ld_x + c0);
+      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + r * ld_x + c0);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = group_max<16>(amax);
+  const float sc = tile_scale(amax, pow2 != 0);
+  const uint32_t lo = e4m3_encode4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+  const uint32_t hi = e4m3_encode4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+  if (valid) {
+    *reinterpret_cast<uint2*>(q + r * ld_q + c0) = make_uint2(lo, hi);
+    if (sub == 0) s[r * tpr + tc] = sc;
+  }
+}
+
 // silu(z) * u in fp32: z / (1 + e^-z) * u, the quotient taken with the hardware reciprocal (1 ulp, like
 // the exponential).  The result is requantised to e4m3, whose rounding absorbs errors of this size
 // except within a few fp32 ulps of a rounding midpoint.

@@ -49,9 +49,17 @@ hipError_t launch_bias_update(const int32_t* topk_idx, long n, int E, float gamm
                               hipStream_t st);
 hipError_t launch_pack(const uint8_t* src, int G, int N, int K, uint8_t* dst, hipStream_t st);
 // part: NULL, or a buffer of part_floats floats for partial logits (the K splits use it when it
-// holds their T * E * splits floats; scores must then be 16-byte aligned)
+// holds their T * E * splits floats; scores must then be 16-byte aligned).
+// xq: NULL, or x's 1x128 quantisation outputs (row length D), written by the small-batch split's
+// finishing kernel; only when router_small_split() holds for the same arguments.
+struct RouterQuant {
+  uint8_t* q;
+  float* s;
+  bool pow2;
+};
+bool router_small_split(int T, int E, int D, const float* part, size_t part_floats);
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, float* part,
-                         size_t part_floats, hipStream_t st);
+                         size_t part_floats, const RouterQuant* xq, hipStream_t st);
 hipError_t launch_route(const float* scores, const float* bias, int T, int E, int k, int G, int gk, int rule,
                         float routed_scale, int32_t* topk_idx, float* topk_w, hipStream_t st);
 size_t permute_scratch_bytes(int n, int E);

@@ -9,51 +9,13 @@
 
 namespace moefp8 {
 
-// One 16-lane group per 128-wide tile, 8 consecutive elements per lane
-// (one 16-byte load for bf16, two for fp32; one 8-byte store of codes).
+// One 16-lane group per 128-wide tile (quant_1x128_tile), 16 tiles per workgroup.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int rows, int cols, int ld_x,
                                                           uint8_t* __restrict__ q, int ld_q, float* __restrict__ s,
                                                           int pow2) {
-  const int tpr = cols >> 7;
-  const long ntiles = (long)rows * tpr;
-  const long tile = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  const bool valid = tile < ntiles;
-  const long r = valid ? tile / tpr : 0;
-  const int tc = valid ? (int)(tile - r * tpr) : 0;
-  const int c0 = tc * 128 + sub * 8;
-  float v[8];
-  if (valid) {
-    if (kBf16) {
-      const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + r * ld_x + c0);
-      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + r * ld_x + c0);
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = group_max<16>(amax);
-  const float sc = tile_scale(amax, pow2 != 0);
-  const uint32_t lo = e4m3_encode4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
-  const uint32_t hi = e4m3_encode4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
-  if (valid) {
-    *reinterpret_cast<uint2*>(q + r * ld_q + c0) = make_uint2(lo, hi);
-    if (sub == 0) s[r * tpr + tc] = sc;
-  }
+  quant_1x128_tile<kBf16>(x, rows, cols, ld_x, q, ld_q, s, pow2, (long)blockIdx.x * 16 + (threadIdx.x >> 4),
+                          threadIdx.x & 15);
 }
 
 // One workgroup per 128x128 block; thread t holds row t/2, columns (t%2)*64 .. +64;

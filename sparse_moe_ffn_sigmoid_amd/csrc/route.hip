@@ -426,10 +426,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
 }
 
 // scores = sigmoid(part[0] + part[1] + ... + part[nz-1]), added in that order; n = T * E (a
-// multiple of 4), one float4 per thread.
-__global__ __launch_bounds__(256) void router_finish_kernel(const float* __restrict__ part, int nz, long n,
-                                                            float* __restrict__ scores) {
-  const long i = blockIdx.x * 256L + threadIdx.x;
+// multiple of 4), float4 i of them.
+__device__ __forceinline__ void finish_logits(const float* __restrict__ part, int nz, long n,
+                                              float* __restrict__ scores, long i) {
   if (4 * i >= n) return;
   v4f a = reinterpret_cast<const v4f*>(part)[i];
   for (int z = 1; z < nz; ++z) a += reinterpret_cast<const v4f*>(part + z * n)[i];
@@ -437,6 +436,27 @@ __global__ __launch_bounds__(256) void router_finish_kernel(const float* __restr
 #pragma unroll
   for (int r = 0; r < 4; ++r) o[r] = 1.0f / (1.0f + expf(-a[r]));
   reinterpret_cast<v4f*>(scores)[i] = o;
+}
+
+__global__ __launch_bounds__(256) void router_finish_kernel(const float* __restrict__ part, int nz, long n,
+                                                            float* __restrict__ scores) {
+  finish_logits(part, nz, n, scores, blockIdx.x * 256L + threadIdx.x);
+}
+
+// The same, with the layer input's 1x128 quantisation in the workgroups past the first nfin
+// (16 tiles each, as quant_1x128_kernel): both are short and latency-bound at small batches,
+// and neither reads what the other writes, so one launch does both.
+__global__ __launch_bounds__(256) void router_finish_quant_kernel(const float* __restrict__ part, int nz, long n,
+                                                                  float* __restrict__ scores, unsigned nfin,
+                                                                  const uint16_t* __restrict__ x, int rows, int cols,
+                                                                  uint8_t* __restrict__ q, float* __restrict__ s,
+                                                                  int pow2) {
+  if (blockIdx.x < nfin) {
+    finish_logits(part, nz, n, scores, blockIdx.x * 256L + threadIdx.x);
+    return;
+  }
+  quant_1x128_tile<true>(x, rows, cols, cols, q, cols, s, pow2, (long)(blockIdx.x - nfin) * 16 + (threadIdx.x >> 4),
+                         threadIdx.x & 15);
 }
 
 // Up to 512 tokens: 16 x 16 tiles of 16 waves; with a partial-logit buffer of kRouterSplit * T * E
@@ -450,14 +470,25 @@ __global__ __launch_bounds__(256) void router_finish_kernel(const float* __restr
 // at 1024, 80 against 109 us at 1536), then 64 x 64 token x expert tiles.
 constexpr int kRouterSplit = 4, kRouterLdsSplitMax = 16;
 
+bool router_small_split(int T, int E, int D, const float* part, size_t part_floats) {
+  return T > 0 && T <= 512 && part && D >= 4096 && part_floats >= (size_t)kRouterSplit * (size_t)T * (size_t)E;
+}
+
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, int T, int E, int D, float* scores, float* part,
-                         size_t part_floats, hipStream_t st) {
+                         size_t part_floats, const RouterQuant* xq, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const long n = (long)T * E;
-  if (T <= 512 && part && D >= 4096 && part_floats >= (size_t)kRouterSplit * n) {
+  if (router_small_split(T, E, D, part, part_floats)) {
     router_splitk_kernel<16, 1, 1, 8, true><<<dim3((T + 15) / 16, E / 16, kRouterSplit), 1024, 0, st>>>(x, w, T, E, D,
                                                                                                          part);
-    router_finish_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(part, kRouterSplit, n, scores);
+    const unsigned nfin = (unsigned)((n / 4 + 255) / 256);
+    if (xq) {
+      const long ntiles = (long)T * (D / 128);
+      router_finish_quant_kernel<<<nfin + (unsigned)((ntiles + 15) / 16), 256, 0, st>>>(
+          part, kRouterSplit, n, scores, nfin, x, T, D, xq->q, xq->s, xq->pow2 ? 1 : 0);
+    } else {
+      router_finish_kernel<<<nfin, 256, 0, st>>>(part, kRouterSplit, n, scores);
+    }
   } else if (T > 512 && part && E % 256 == 0 && D % 64 == 0) {
     const int tiles = ((T + 127) / 128) * (E / 256);
     int nz = std::min(kRouterLdsSplitMax, std::max(1, 256 / tiles));

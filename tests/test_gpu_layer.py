@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import synth
-from oracle import route
+from oracle import quant, route
 
 pytestmark = pytest.mark.gpu
 
@@ -146,21 +146,37 @@ def test_single_token_and_empty_batch(tiny):
 ROUTER_SPLIT = synth.MoeShape("router_split", 21, 512, 4096, 128, 16, 4, 1, 128, 4, 2)
 
 
-@pytest.mark.parametrize("T", [1, 64, 512])
-def test_forward_router_scores_split_over_k(T):
+@pytest.mark.parametrize("T,ue8m0", [(1, False), (64, False), (512, False), (64, True)])
+def test_forward_router_scores_split_over_k(T, ue8m0):
     """Batches of up to 512 tokens with a hidden dimension of 4096 or more: the forward's router
     splits the hidden dimension over four workgroups and adds their partial logits in a fixed
-    order.  Its scores against the oracle's (the bound of the single-pass router), and the same
-    routing as the oracle's except at near-ties."""
+    order; the layer input's 1x128 quantisation runs in the same launch as that sum (fp32 or
+    power-of-two scales).  Its scores against the oracle's (the bound of the single-pass router),
+    the same routing as the oracle's except at near-ties, and the layer output."""
     s = dataclasses.replace(ROUTER_SPLIT, tokens=T)
-    say(f"forward router with the hidden dimension split: T={T}, hidden {s.hidden}")
-    layer = Layer(s)
+    say(f"forward router with the hidden dimension split: T={T}, hidden {s.hidden}, ue8m0 {ue8m0}")
+    layer = Layer(s, ue8m0=ue8m0)
     xb = synth.gen_x(s)
     got = _run(layer, xb)
     want = route.sigmoid_scores(route.router_logits(synth.bf16_bits_to_f32(xb),
                                                     synth.bf16_bits_to_f32(synth.gen_router_w(s))))
     assert np.abs(got["scores"] - want).max() <= 2e-5
     _compare_router_run(layer, xb, got)
+    # x's codes and scales, read from the forward's workspace (after the bf16 normalised-rows
+    # region, 256-byte aligned: codes [T][hidden], then scales [T][hidden / 128]), bit-exact
+    # against the oracle's quantiser; the workspace is filled with 0xA5 first
+    ws = moe.alloc_workspace(T, layer.cfg, DEV).fill_(0xA5)
+    moe.moe_ffn_forward(to_dev(xb), layer.cfg, layer.weights, workspace=ws)
+    torch.cuda.synchronize()
+    d = s.hidden
+    align = lambda v: (v + 255) // 256 * 256
+    o_q = align(T * d * 2)
+    o_s = o_q + align(T * d)
+    wsn = ws.cpu().numpy()
+    want_q, want_s = quant.quant_1x128(synth.bf16_bits_to_f32(xb), ue8m0)
+    assert np.array_equal(wsn[o_q:o_q + T * d].reshape(T, d), want_q)
+    assert np.array_equal(wsn[o_s:o_s + T * (d // 128) * 4].view(np.float32).reshape(T, d // 128).view(np.uint32),
+                          np.asarray(want_s, np.float32).view(np.uint32))
 
 
 ROUTER_LDS = synth.MoeShape("router_lds", 22, 1100, 1152, 128, 256, 8, 1, 128, 8, 4)
