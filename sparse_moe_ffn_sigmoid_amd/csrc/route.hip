@@ -462,8 +462,9 @@ __global__ __launch_bounds__(256) void router_finish_quant_kernel(const float* _
 // Up to 512 tokens: 16 x 16 tiles of 16 waves; with a partial-logit buffer of kRouterSplit * T * E
 // floats (the forward lends one) and a hidden dimension of at least 4096 the hidden dimension is
 // also split 4 ways (at T = 64: 256 workgroups instead of 64).  Larger batches with a
-// partial-logit buffer (the forward's) and 256k experts: router_lds_kernel, its K range split over
-// up to 16 workgroups so that the grid fills the chip (T = 4096: 32 token tiles x 8); V3 router,
+// partial-logit buffer (the forward's) and a multiple of 256 experts: router_lds_kernel, its K
+// range split over up to 16 workgroups so that the grid fills the chip (T = 4096: 32 token tiles
+// x 8); V3 router,
 // route + permutation stage: T = 1280 0.079 -> 0.050 ms, 4096 0.083 -> 0.067, 16384 0.271 ->
 // 0.134.  Otherwise (moe_route's router, other expert counts) the 16 x 16 tiles up to 1024 tokens
 // (at T = 640 the route + permutation stage took 68 against 80 us with the 64 x 64 tiles, equal

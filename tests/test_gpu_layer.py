@@ -190,10 +190,11 @@ ROUTER_LDS = synth.MoeShape("router_lds", 22, 1100, 1152, 128, 256, 8, 1, 128, 8
     (8192, 256, 1024, False),   # 64 token tiles x 4 expert tiles: no split, the sigmoid in the kernel
 ])
 def test_forward_router_scores_large_batch(T, hidden, E, whole):
-    """Batches above 512 tokens with 256k experts: the forward's router stages 128 tokens x 256
-    experts through LDS, its hidden dimension split over workgroups whose partial logits are added
-    in a fixed order.  Every score against the oracle's (the bound of the single-pass router); the
-    layer against the oracle on every token, or on the first and last 128 tokens."""
+    """Batches above 512 tokens with a multiple of 256 experts: the forward's router stages 128
+    tokens x 256 experts through LDS, its hidden dimension split over workgroups whose partial
+    logits are added in a fixed order.  Every score against the oracle's (the bound of the
+    single-pass router); the layer against the oracle on every token, or on the first and last 128
+    tokens."""
     s = dataclasses.replace(ROUTER_LDS, tokens=T, hidden=hidden, n_experts=E)
     say(f"forward router, LDS-staged: T={T}, hidden {hidden}, E={E}")
     layer = Layer(s)
